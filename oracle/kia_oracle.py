@@ -1,0 +1,334 @@
+"""K-interval attention: plain fp64 CPU oracle.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check of the graft
+entry module and the benchmark's CPU-baseline leg may import or run this
+file.  It shares no code, constant table or helper with the HIP library, and
+the library never calls it.
+
+What it computes follows "Pretraining Transformers with Quantized Softmax in
+Attention" (paperlayer digest of the paper):
+
+* Operator family (section 3, "Operator family"; App. A "Operator definitions
+  and edge cases"): per causal row of scores, a row calibration sets K+1 grid
+  values exp(-j h); each score is reconstructed from the grid (LERP or
+  Nearest), the reconstructed weights are normalised, P_j = w_j / W, and
+  O = P V.  Future positions get no weight; the row is shifted by its maximum
+  before exponentiation.
+* Calibration (section 3 "Calibration"; App. A): MinMax takes h = (max-min)/K
+  from the row span; FWM takes h = tau/K anchored at the row maximum and gives
+  zero weight below max - tau.  Spans below eps = 1e-12 take a separate branch.
+* Reconstruction (section 3 "Reconstruction", Figure 1; App. A): LERP
+  interpolates linearly between the two grid values around a score; Nearest
+  gives every score the grid value it rounds to, so one bin shares one weight.
+* Gradients (section 3 "Calibration gradients", "Surrogate placement";
+  App. B "Gradient derivations"): the normalisation Jacobian turns dL/dP into
+  dL/dw; the full calibration gradient differentiates through the shifted
+  scores, the grid values and h, i.e. through the row max and min, and its
+  per-key partials sum to zero; detach drops the extremum terms; max-only and
+  min-only keep one of them (App. F).  Nearest uses the LERP derivative as its
+  surrogate; Weight-STE evaluates the normalisation Jacobian at the hard
+  weights, Prob-STE at the LERP probabilities and normaliser.
+
+Readings where the pages leave a step open (each is listed in the design doc):
+  R1  Nearest rounds to the nearest grid point j*h (K+1 levels); a score
+      exactly half-way rounds up in u, i.e. r = floor(u + 1/2).
+  R2  LERP uses segment i = min(floor(u), K-1): at a knot the right-hand
+      segment's derivative is used, the row minimum (u = K) uses segment K-1.
+  R3  Ties for the row max / min: the smallest key index is the extremum.
+  R4  Spans below eps: w = 1 for every causal key (uniform P); the backward is
+      the h -> 0 limit dS = P (dP - delta) with no calibration terms.
+  R5  Under FWM a key is in the window iff s >= max - tau (u <= K).
+  R6  detach holds m (as the shift and inside h) and n constant; max-only
+      holds n constant; min-only holds m constant.  Under FWM the min plays
+      no role, so min-only equals detach and max-only equals full.
+  R7  Scores are Q.K / sqrt(d); key t is causal for query t.
+  R8  P1 (zero-sum projection of the detached gradient, App. B; section 5.1):
+      dS <- dS_detach - mean over the row's causal keys.
+
+Parity: every function below is pinned by the CPU tests (closed forms,
+brute force, finite differences, an autograd re-expression, the softmax
+limit, the zero-sum identity); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+MINMAX, FWM = 0, 1
+LERP, NEAREST = 0, 1
+WEIGHT_STE, PROB_STE = 0, 1
+FULL, DETACH, MAX_ONLY, MIN_ONLY, P1 = 0, 1, 2, 3, 4
+
+EPS_SPAN = 1e-12  # App. A: branches for spans above / below 1e-12
+
+
+@dataclass(frozen=True)
+class Params:
+    K: int                     # number of intervals; the grid has K+1 values
+    tau: float = 6.0           # FWM window in nats
+    calibration: int = MINMAX
+    reconstruction: int = LERP
+    surrogate: int = WEIGHT_STE
+    grad_rule: int = FULL
+
+    def carries_max(self) -> bool:
+        return self.grad_rule in (FULL, MAX_ONLY)
+
+    def carries_min(self) -> bool:
+        return self.grad_rule in (FULL, MIN_ONLY) and self.calibration == MINMAX
+
+
+# ---------------------------------------------------------------------------
+# one causal row
+# ---------------------------------------------------------------------------
+
+def row_scores(q_t: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    """s_j = Q_t . K_j / sqrt(d) over the causal keys (reading R7)."""
+    d = keys.shape[1]
+    return (keys.astype(np.float64) @ q_t.astype(np.float64)) / np.sqrt(d)
+
+
+@dataclass
+class Calibration:
+    m: float          # row max
+    a: int            # its key (smallest index on ties, R3)
+    n: float          # row min
+    b: int
+    h: float          # grid width (0 in the degenerate branch)
+    degenerate: bool  # MinMax span below eps (R4)
+
+
+def calibrate(s: np.ndarray, p: Params) -> Calibration:
+    """Row calibration: MinMax h = span/K, FWM h = tau/K (section 3; App. A)."""
+    a = int(np.argmax(s))   # numpy returns the first maximal index
+    b = int(np.argmin(s))
+    m, n = float(s[a]), float(s[b])
+    if p.calibration == MINMAX:
+        span = m - n
+        if span < EPS_SPAN:
+            return Calibration(m, a, n, b, 0.0, True)
+        return Calibration(m, a, n, b, span / p.K, False)
+    return Calibration(m, a, n, b, p.tau / p.K, False)
+
+
+def grid(h: float, K: int) -> np.ndarray:
+    """The K+1 grid values exp(-j h), j = 0..K."""
+    return np.exp(-h * np.arange(K + 1, dtype=np.float64))
+
+
+@dataclass
+class Recon:
+    """Per-key reconstruction state of one row."""
+    u: np.ndarray      # (m - s)/h, distance below the max in grid steps
+    uc: np.ndarray     # u clamped to K (rounding guard, not differentiated)
+    mask: np.ndarray   # 1 in the window (always 1 for MinMax)
+    i: np.ndarray      # LERP segment
+    f: np.ndarray      # position inside the segment
+    r: np.ndarray      # Nearest grid point
+    g: np.ndarray      # the grid
+    wL: np.ndarray     # LERP weights
+    wN: np.ndarray     # Nearest weights
+
+
+def reconstruct(s: np.ndarray, m: float, h: float, p: Params, clamp: bool = True) -> Recon:
+    """Grid reconstruction of a row (section 3 "Reconstruction"; App. A).
+
+    ``clamp=False`` keeps u unclamped and lets the end segments extend
+    linearly; it exists for derivative checks that move a score past the row
+    extremes while the extremes are held fixed.
+    """
+    K = p.K
+    u = (m - s) / h
+    if p.calibration == FWM:
+        mask = (u <= K).astype(np.float64)                     # R5
+    else:
+        mask = np.ones_like(u)
+    uc = np.minimum(u, float(K)) if clamp else u.copy()
+    g = grid(h, K)
+    i = np.clip(np.floor(uc), 0, K - 1).astype(np.int64)      # R2
+    f = uc - i
+    wL = mask * ((1.0 - f) * g[i] + f * g[i + 1])               # linear interpolation
+    r = np.clip(np.floor(uc + 0.5), 0, K).astype(np.int64)    # R1
+    wN = mask * g[r]
+    return Recon(u, uc, mask, i, f, r, g, wL, wN)
+
+
+@dataclass
+class RowForward:
+    s: np.ndarray
+    cal: Calibration
+    rec: Recon | None
+    w: np.ndarray       # forward weights (hard for Nearest)
+    W: float
+    P: np.ndarray
+    wL: np.ndarray      # LERP weights (= w for LERP)
+    WL: float
+
+
+def row_forward(s: np.ndarray, p: Params) -> RowForward:
+    cal = calibrate(s, p)
+    if cal.degenerate:                                          # R4
+        w = np.ones_like(s)
+        W = float(w.sum())
+        return RowForward(s, cal, None, w, W, w / W, w, W)
+    rec = reconstruct(s, cal.m, cal.h, p)
+    w = rec.wL if p.reconstruction == LERP else rec.wN          # Nearest computed directly
+    W = float(w.sum())
+    WL = float(rec.wL.sum())
+    return RowForward(s, cal, rec, w, W, w / W, rec.wL, WL)
+
+
+@dataclass
+class RowBackward:
+    dS: np.ndarray      # dL/ds over the causal keys, calibration terms included
+    dS_direct: np.ndarray
+    gt: np.ndarray      # dL/dw at the evaluation point
+    Cm: float           # calibration sum routed to the argmax key
+    Cn: float           # calibration sum routed to the argmin key
+    delta: float
+    We: float
+
+
+def row_backward(fw: RowForward, dP: np.ndarray, p: Params) -> RowBackward:
+    """Score gradient of one row given dP_j = dO_t . V_j (App. B)."""
+    cal, rec = fw.cal, fw.rec
+    if cal.degenerate:                                          # R4: softmax limit
+        delta = float(np.dot(fw.P, dP))
+        dS = fw.P * (dP - delta)
+        gt = (dP - delta) / fw.W
+        return RowBackward(dS, dS.copy(), gt, 0.0, 0.0, delta, fw.W)
+
+    # Evaluation point of the normalisation Jacobian (section 3 "Surrogate placement")
+    if p.reconstruction == NEAREST and p.surrogate == PROB_STE:
+        Pe, We = rec.wL / fw.WL, fw.WL
+    else:
+        Pe, We = fw.P, fw.W
+    delta = float(np.dot(Pe, dP))
+    gt = (dP - delta) / We                                      # dL/dw_j
+
+    # LERP derivatives (the surrogate for Nearest), zero outside the window
+    g, i, f, h, K = rec.g, rec.i, rec.f, cal.h, p.K
+    dw_du = rec.mask * (g[i + 1] - g[i])
+    dw_dh = rec.mask * ((1.0 - f) * (-i * g[i]) + f * (-(i + 1) * g[i + 1]))
+    du_ds = -1.0 / h
+    du_dm = 1.0 / h
+    du_dh = -rec.uc / h
+    dw_dh_total = dw_du * du_dh + dw_dh          # w's dependence on h at fixed s and m
+
+    dS_direct = gt * dw_du * du_ds
+    if p.calibration == MINMAX:
+        dh_dm, dh_dn = 1.0 / K, -1.0 / K
+        Cm = float(np.sum(gt * (dw_du * du_dm + dw_dh_total * dh_dm)))
+        Cn = float(np.sum(gt * dw_dh_total * dh_dn))
+    else:
+        Cm = float(np.sum(gt * dw_du * du_dm))
+        Cn = 0.0
+
+    dS = dS_direct.copy()
+    if p.grad_rule == P1:                                       # R8
+        dS = dS - dS.mean()
+    else:
+        if p.carries_max():
+            dS[cal.a] += Cm
+        if p.carries_min():
+            dS[cal.b] += Cn
+    return RowBackward(dS, dS_direct, gt, Cm, Cn, delta, We)
+
+
+# ---------------------------------------------------------------------------
+# one (batch, head) slice
+# ---------------------------------------------------------------------------
+
+def head_forward(Q, Kt, V, p: Params, rows=None):
+    """Forward over one head: Q, K, V are [T, d].  Returns a dict with O
+    ([T, d], rows not asked for are NaN), the row statistics, and the
+    per-row records of the rows asked for (``rows`` None means all)."""
+    T, d = Q.shape
+    rows = range(T) if rows is None else rows
+    O = np.full((T, d), np.nan)
+    st = {k: np.full(T, np.nan) for k in ("m", "n", "h", "W", "WL")}
+    st["a"] = np.full(T, -1, dtype=np.int64)
+    st["b"] = np.full(T, -1, dtype=np.int64)
+    st["degenerate"] = np.zeros(T, dtype=bool)
+    recs = {}
+    V64 = V.astype(np.float64)
+    for t in rows:
+        s = row_scores(Q[t], Kt[: t + 1])
+        fw = row_forward(s, p)
+        O[t] = fw.P @ V64[: t + 1]
+        c = fw.cal
+        st["m"][t], st["n"][t], st["h"][t] = c.m, c.n, c.h
+        st["a"][t], st["b"][t], st["degenerate"][t] = c.a, c.b, c.degenerate
+        st["W"][t], st["WL"][t] = fw.W, fw.WL
+        recs[t] = fw
+    return {"O": O, "stats": st, "rows": recs}
+
+
+def head_backward(Q, Kt, V, dO, p: Params, keep_rows: bool = False):
+    """Forward + backward over one head.  Returns dQ, dK, dV ([T, d]) and
+    per-row Cm, Cn, the row sum and L1 norm of dS; ``keep_rows`` also returns
+    the per-row forward/backward records."""
+    T, d = Q.shape
+    scale = 1.0 / np.sqrt(d)
+    Q64, K64, V64, dO64 = (x.astype(np.float64) for x in (Q, Kt, V, dO))
+    dQ = np.zeros((T, d))
+    dK = np.zeros((T, d))
+    dV = np.zeros((T, d))
+    Cm = np.zeros(T)
+    Cn = np.zeros(T)
+    dS_sum = np.zeros(T)
+    dS_l1 = np.zeros(T)
+    recs = {}
+    for t in range(T):
+        s = row_scores(Q64[t], K64[: t + 1])
+        fw = row_forward(s, p)
+        dP = V64[: t + 1] @ dO64[t]
+        bw = row_backward(fw, dP, p)
+        dQ[t] = (bw.dS @ K64[: t + 1]) * scale
+        dK[: t + 1] += np.outer(bw.dS, Q64[t]) * scale
+        dV[: t + 1] += np.outer(fw.P, dO64[t])               # forward (hard) P
+        Cm[t], Cn[t] = bw.Cm, bw.Cn
+        dS_sum[t] = bw.dS.sum()
+        dS_l1[t] = np.abs(bw.dS).sum()
+        if keep_rows:
+            recs[t] = (fw, bw)
+    out = {"dQ": dQ, "dK": dK, "dV": dV, "Cm": Cm, "Cn": Cn,
+           "dS_sum": dS_sum, "dS_l1": dS_l1}
+    if keep_rows:
+        out["rows"] = recs
+    return out
+
+
+# ---------------------------------------------------------------------------
+# whole [B, H, T, d] tensors
+# ---------------------------------------------------------------------------
+
+def forward(q, k, v, p: Params):
+    """O and row statistics for [B, H, T, d] inputs."""
+    B, H, T, d = q.shape
+    O = np.zeros((B, H, T, d))
+    stats = None
+    for bi in range(B):
+        for hi in range(H):
+            r = head_forward(q[bi, hi], k[bi, hi], v[bi, hi], p)
+            O[bi, hi] = r["O"]
+            if stats is None:
+                stats = {key: np.zeros((B, H, T), dtype=val.dtype) for key, val in r["stats"].items()}
+            for key, val in r["stats"].items():
+                stats[key][bi, hi] = val
+    return O, stats
+
+
+def backward(q, k, v, do, p: Params):
+    """dQ, dK, dV for [B, H, T, d] inputs, plus per-row calibration sums."""
+    B, H, T, d = q.shape
+    out = {key: np.zeros((B, H, T, d)) for key in ("dQ", "dK", "dV")}
+    for key in ("Cm", "Cn", "dS_sum", "dS_l1"):
+        out[key] = np.zeros((B, H, T))
+    for bi in range(B):
+        for hi in range(H):
+            r = head_backward(q[bi, hi], k[bi, hi], v[bi, hi], do[bi, hi], p)
+            for key in out:
+                out[key][bi, hi] = r[key]
+    return out
