@@ -1,0 +1,169 @@
+/*
+ * kia.h - C ABI of the K-interval attention library (libkia.so, gfx950).
+ *
+ * K-interval attention is the attention operator of "Pretraining Transformers
+ * with Quantized Softmax in Attention" (paperlayer digest of the paper).  Per
+ * causal row of scores s_j = Q_t . K_j / sqrt(d) (key t included):
+ *   - a row calibration sets a grid of K+1 values exp(-j h): MinMax takes
+ *     h = (max - min) / K from the row span, FWM takes h = tau / K anchored at
+ *     the row max and gives zero weight below max - tau (section 3
+ *     "Calibration"; App. A "Operator definitions and edge cases");
+ *   - each score is reconstructed from the grid, by linear interpolation
+ *     between the two grid values around it (LERP) or by the grid value it
+ *     rounds to (Nearest) (section 3 "Reconstruction", Figure 1; App. A);
+ *   - weights are normalised, P_j = w_j / W, and O = P V (App. A);
+ *   - the backward applies the normalisation Jacobian and carries the
+ *     calibration derivatives through the row max and min (full), drops them
+ *     (detach) or keeps one of them (max-only / min-only); for Nearest the
+ *     LERP derivative is the surrogate, with the Jacobian evaluated at the hard
+ *     weights (Weight-STE) or at the LERP probabilities (Prob-STE) (section 3
+ *     "Calibration gradients", "Surrogate placement"; App. B "Gradient
+ *     derivations"; App. F for max-only / min-only).
+ * Spans below 1e-12 take the degenerate branch (App. A, Table S1): uniform
+ * weights forward, the softmax-limit gradient dS = P (dP - delta) backward.
+ *
+ * Conventions for every entry point:
+ *   - Tensors are fp32, contiguous [B, H, T, d], d in {64, 128}; tensor
+ *     pointers are DEVICE pointers, 16-byte aligned, owned by the caller.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  The
+ *     library launches only on that stream, never synchronises, never
+ *     allocates, and keeps no mutable global state: calls are thread-safe.
+ *   - Every argument check happens before the first launch; on error nothing
+ *     is launched and a non-zero kia_status is returned.  Launch failures are
+ *     reported as KIA_ERR_HIP.  Output contents are unspecified on error.
+ *   - Results are deterministic: no atomics; repeated calls give identical
+ *     bits, and a (b, h) slice does not depend on the rest of the batch.
+ */
+#ifndef KIA_H
+#define KIA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kia_status {
+    KIA_OK = 0,
+    KIA_ERR_NULL = 1,      /* a required pointer is NULL */
+    KIA_ERR_SHAPE = 2,     /* B, H, T < 1, d not in {64, 128}, or sizes overflow */
+    KIA_ERR_PARAM = 3,     /* flag out of range, n_intervals < 1, tau <= 0 under FWM */
+    KIA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned */
+    KIA_ERR_BUFFER = 5,    /* stats or workspace smaller than the size query returns */
+    KIA_ERR_HIP = 6        /* a kernel launch failed */
+} kia_status;
+
+enum { KIA_CAL_MINMAX = 0, KIA_CAL_FWM = 1 };
+enum { KIA_REC_LERP = 0, KIA_REC_NEAREST = 1 };
+enum { KIA_STE_WEIGHT = 0, KIA_STE_PROB = 1 };  /* read only for Nearest */
+enum { KIA_GRAD_FULL = 0, KIA_GRAD_DETACH = 1, KIA_GRAD_MAX_ONLY = 2, KIA_GRAD_MIN_ONLY = 3 };
+
+/* Operator flags.  n_intervals is the method's K (grid of K+1 values); it is
+ * named so it cannot be mistaken for the key tensor.  tau is the FWM window
+ * in nats (ignored for MinMax).  The forward never reads grad_rule, and reads
+ * surrogate only to decide whether to keep the Prob-STE extras, so forwards
+ * that differ only in those flags are bitwise identical.  Under FWM the row
+ * min plays no role: MIN_ONLY behaves as DETACH and MAX_ONLY as FULL. */
+typedef struct kia_params {
+    int32_t n_intervals;     /* 1 .. 65536 */
+    float tau;               /* > 0 and finite under FWM */
+    int32_t calibration;     /* KIA_CAL_* */
+    int32_t reconstruction;  /* KIA_REC_* */
+    int32_t surrogate;       /* KIA_STE_* */
+    int32_t grad_rule;       /* KIA_GRAD_* */
+} kia_params;
+
+/* Byte offsets of the forward -> backward state inside `stats`.  The forward
+ * materialises every causal score once (fp32, tiles of 32 queries x 32 keys,
+ * per (b, h) slice the tiles (qt, kt), kt <= qt, in order qt*(qt+1)/2 + kt);
+ * the backward reads them instead of recomputing Q K^T.  Row arrays are
+ * [B*H*T]: max m, min n (fp32), argmax a, argmin b (int32, smallest key index
+ * on ties), normaliser W and LERP normaliser WL (fp32).  o_lerp ([B,H,T,d]
+ * fp32, the LERP-probability output used by the Prob-STE backward) is present
+ * only for Nearest + Prob-STE (else o_lerp == 0). */
+typedef struct kia_stats_layout {
+    size_t total_bytes;
+    size_t scores;
+    size_t row_m, row_n, row_a, row_b, row_w, row_wl;
+    size_t o_lerp;
+    int64_t tiles_per_head;
+} kia_stats_layout;
+
+/* Byte offsets inside the backward workspace: the hard probabilities P and
+ * the direct score gradient dS (calibration terms not included) as tiles in
+ * key-major order (per (b, h): tile (qt, kt) at the same index as the score
+ * tiles), and the per-row calibration terms actually routed by the gradient
+ * rule to the argmax key (cm) and the argmin key (cn), fp32 [B*H*T]. */
+typedef struct kia_workspace_layout {
+    size_t total_bytes;
+    size_t probs;
+    size_t dscores;
+    size_t row_cm, row_cn;
+} kia_workspace_layout;
+
+/* Size queries.  Return 0 on invalid arguments (same checks as the calls). */
+size_t kia_stats_bytes(const kia_params* p, int B, int H, int T, int d);
+size_t kia_workspace_bytes(const kia_params* p, int B, int H, int T, int d);
+kia_status kia_stats_layout_query(const kia_params* p, int B, int H, int T, int d,
+                                  kia_stats_layout* out);
+kia_status kia_workspace_layout_query(const kia_params* p, int B, int H, int T, int d,
+                                      kia_workspace_layout* out);
+
+/* Forward: O = P V with P the normalised K-interval weights (App. A).
+ * q, k, v: inputs [B,H,T,d]; o: output [B,H,T,d]; stats: output, at least
+ * kia_stats_bytes(...) bytes, read by kia_backward with the same p and shape. */
+kia_status kia_forward(const kia_params* p, int B, int H, int T, int d,
+                       const float* q, const float* k, const float* v, float* o,
+                       void* stats, size_t stats_bytes, void* stream);
+
+/* Backward: dQ, dK, dV of sum(dO * O) under p's gradient rule and surrogate
+ * placement (section 3; App. B).  o and stats must come from kia_forward with
+ * the same q, k, v, p and shape.  ws: scratch of kia_workspace_bytes(...)
+ * bytes; on return it holds the tiles and row terms kia_workspace_layout
+ * describes.  dq, dk, dv: outputs [B,H,T,d]. */
+kia_status kia_backward(const kia_params* p, int B, int H, int T, int d,
+                        const float* q, const float* k, const float* v,
+                        const float* o, const float* d_o,
+                        const void* stats, size_t stats_bytes,
+                        float* dq, float* dk, float* dv,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Optional extras for the two calls above.  events: NULL or an array of
+ * hipEvent_t (as void*) recorded on `stream` around each kernel: forward
+ * uses 2 (start/end of its one kernel), backward 6 (around its three kernels,
+ * in launch order).  idx_dump (forward only): NULL or int32 [B,H,T,T]; for
+ * every causal pair the kernel writes the grid index it used (the LERP
+ * segment, or the Nearest grid point), -1 for keys outside the FWM window;
+ * non-causal entries are left untouched. */
+typedef struct kia_ext {
+    void* const* events;
+    int32_t n_events;
+    int32_t* idx_dump;
+} kia_ext;
+
+kia_status kia_forward_ext(const kia_params* p, int B, int H, int T, int d,
+                           const float* q, const float* k, const float* v, float* o,
+                           void* stats, size_t stats_bytes, void* stream, const kia_ext* ext);
+kia_status kia_backward_ext(const kia_params* p, int B, int H, int T, int d,
+                            const float* q, const float* k, const float* v,
+                            const float* o, const float* d_o,
+                            const void* stats, size_t stats_bytes,
+                            float* dq, float* dk, float* dv,
+                            void* ws, size_t ws_bytes, void* stream, const kia_ext* ext);
+
+/* Expand a tile buffer (scores from stats, or probs / dscores from the
+ * workspace) into a dense fp32 [B,H,T,T] matrix for inspection.  key_major:
+ * 0 for the score tiles, 1 for the workspace tiles.  Only causal entries are
+ * written.  Device pointers; launches on `stream`. */
+kia_status kia_tiles_to_dense(int B, int H, int T, const float* tiles, int key_major,
+                              float* dense, void* stream);
+
+const char* kia_status_str(kia_status s);
+int32_t kia_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KIA_H */

@@ -1,0 +1,190 @@
+"""K-interval attention on AMD Instinct MI355X (gfx950).
+
+A thin binding over libkia.so (C ABI in include/kia.h).  PyTorch only
+supplies device memory and the current stream; every step of the operator
+runs in the library's HIP kernels.  The functions keep the C names:
+
+    o, stats = kia_forward(q, k, v, params)
+    dq, dk, dv, ws = kia_backward(q, k, v, o, do, stats, params)
+
+with q, k, v, o, do fp32 CUDA tensors of shape [B, H, T, d], d in {64, 128}.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+from . import _lib
+from ._lib import KiaExt, KiaParams, KiaStatsLayout, KiaWorkspaceLayout
+
+CAL = {"minmax": 0, "fwm": 1}
+REC = {"lerp": 0, "nearest": 1}
+STE = {"weight": 0, "prob": 1}
+RULE = {"full": 0, "detach": 1, "max_only": 2, "min_only": 3}
+
+
+class KiaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = _lib.load().kia_status_str(status).decode()
+        super().__init__(f"{where}: {msg} (status {status})")
+        self.status = status
+
+
+@dataclass(frozen=True)
+class Params:
+    """Operator flags; K is the number of intervals (K+1 grid values)."""
+    K: int
+    tau: float = 6.0
+    calibration: str = "minmax"
+    reconstruction: str = "lerp"
+    surrogate: str = "weight"
+    grad_rule: str = "full"
+
+    def c(self) -> KiaParams:
+        def pick(table, v):
+            return table[v] if isinstance(v, str) else int(v)
+        return KiaParams(int(self.K), float(self.tau), pick(CAL, self.calibration),
+                         pick(REC, self.reconstruction), pick(STE, self.surrogate),
+                         pick(RULE, self.grad_rule))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _shape(q):
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, T, d]")
+    return tuple(int(x) for x in q.shape)
+
+
+def _check(t, name, shape=None):
+    torch = _torch()
+    if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 GPU tensor")
+    if shape is not None and tuple(t.shape) != shape:
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ext(events, idx_dump):
+    if events is None and idx_dump is None:
+        return None
+    ext = KiaExt()
+    if events is not None:
+        arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(int(e)) for e in events])
+        ext.events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+        ext.n_events = len(events)
+        ext._keep = arr
+    if idx_dump is not None:
+        ext.idx_dump = ctypes.c_void_p(idx_dump.data_ptr())
+    return ext
+
+
+def kia_stats_bytes(params: Params, B, H, T, d) -> int:
+    return int(_lib.load().kia_stats_bytes(ctypes.byref(params.c()), B, H, T, d))
+
+
+def kia_workspace_bytes(params: Params, B, H, T, d) -> int:
+    return int(_lib.load().kia_workspace_bytes(ctypes.byref(params.c()), B, H, T, d))
+
+
+def kia_stats_layout_query(params: Params, B, H, T, d) -> KiaStatsLayout:
+    out = KiaStatsLayout()
+    st = _lib.load().kia_stats_layout_query(ctypes.byref(params.c()), B, H, T, d, ctypes.byref(out))
+    if st:
+        raise KiaError(st, "kia_stats_layout_query")
+    return out
+
+
+def kia_workspace_layout_query(params: Params, B, H, T, d) -> KiaWorkspaceLayout:
+    out = KiaWorkspaceLayout()
+    st = _lib.load().kia_workspace_layout_query(ctypes.byref(params.c()), B, H, T, d, ctypes.byref(out))
+    if st:
+        raise KiaError(st, "kia_workspace_layout_query")
+    return out
+
+
+def kia_forward(q, k, v, params: Params, o=None, stats=None, stream=None, events=None, idx_dump=None):
+    """O = P V with K-interval weights.  Returns (o, stats); stats is a uint8
+    device buffer holding the forward -> backward state."""
+    torch = _torch()
+    B, H, T, d = _shape(q)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, nm, (B, H, T, d))
+    lib = _lib.load()
+    cp = params.c()
+    nbytes = int(lib.kia_stats_bytes(ctypes.byref(cp), B, H, T, d))
+    if nbytes == 0:
+        raise KiaError(3 if d in (64, 128) else 2, "kia_stats_bytes")
+    if o is None:
+        o = torch.empty_like(q)
+    if stats is None:
+        stats = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    if idx_dump is not None and (idx_dump.dtype != torch.int32 or idx_dump.numel() != B * H * T * T):
+        raise ValueError("idx_dump must be int32 with B*H*T*T elements")
+    ext = _ext(events, idx_dump)
+    args = (ctypes.byref(cp), B, H, T, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+            stats.data_ptr(), stats.numel(), _stream(stream))
+    st = lib.kia_forward_ext(*args, ctypes.byref(ext)) if ext is not None else lib.kia_forward(*args)
+    if st:
+        raise KiaError(st, "kia_forward")
+    return o, stats
+
+
+def kia_backward(q, k, v, o, do, stats, params: Params, dq=None, dk=None, dv=None, ws=None,
+                 stream=None, events=None):
+    """dQ, dK, dV of sum(do * o).  Returns (dq, dk, dv, ws); ws is the
+    workspace (uint8 device buffer) whose tiles kia_workspace_layout_query
+    describes."""
+    torch = _torch()
+    B, H, T, d = _shape(q)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _check(t, nm, (B, H, T, d))
+    lib = _lib.load()
+    cp = params.c()
+    wbytes = int(lib.kia_workspace_bytes(ctypes.byref(cp), B, H, T, d))
+    if wbytes == 0:
+        raise KiaError(3, "kia_workspace_bytes")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    if ws is None:
+        ws = torch.empty(wbytes, dtype=torch.uint8, device=q.device)
+    ext = _ext(events, None)
+    args = (ctypes.byref(cp), B, H, T, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+            do.data_ptr(), stats.data_ptr(), stats.numel(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+            ws.data_ptr(), ws.numel(), _stream(stream))
+    st = lib.kia_backward_ext(*args, ctypes.byref(ext)) if ext is not None else lib.kia_backward(*args)
+    if st:
+        raise KiaError(st, "kia_backward")
+    return dq, dk, dv, ws
+
+
+def kia_tiles_to_dense(B, H, T, tiles, key_major: bool, dense=None, stream=None):
+    """Expand a tile buffer (a uint8/float view starting at the tiles) into a
+    dense [B, H, T, T] fp32 tensor; non-causal entries keep dense's content
+    (zeros when dense is allocated here)."""
+    torch = _torch()
+    if dense is None:
+        dense = torch.zeros((B, H, T, T), dtype=torch.float32, device=tiles.device)
+    st = _lib.load().kia_tiles_to_dense(B, H, T, tiles.data_ptr(), 1 if key_major else 0,
+                                        dense.data_ptr(), _stream(stream))
+    if st:
+        raise KiaError(st, "kia_tiles_to_dense")
+    return dense
+
+
+def kia_abi_version() -> int:
+    return int(_lib.load().kia_abi_version())
+
+
+__all__ = ["Params", "KiaError", "kia_forward", "kia_backward", "kia_stats_bytes",
+           "kia_workspace_bytes", "kia_stats_layout_query", "kia_workspace_layout_query",
+           "kia_tiles_to_dense", "kia_abi_version"]

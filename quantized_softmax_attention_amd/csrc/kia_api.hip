@@ -1,0 +1,274 @@
+// C ABI of libkia: argument checks, buffer layouts and kernel dispatch.
+// Every check runs before the first launch; the library never allocates,
+// never synchronises and keeps no mutable global state.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/kia.h"
+#include "kia_common.hpp"
+#include "kia_kernels.hpp"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxIntervals = 65536;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+kia_status check_params(const kia_params* p) {
+    if (!p) return KIA_ERR_NULL;
+    if (p->n_intervals < 1 || p->n_intervals > kMaxIntervals) return KIA_ERR_PARAM;
+    if (p->calibration != KIA_CAL_MINMAX && p->calibration != KIA_CAL_FWM) return KIA_ERR_PARAM;
+    if (p->reconstruction != KIA_REC_LERP && p->reconstruction != KIA_REC_NEAREST) return KIA_ERR_PARAM;
+    if (p->surrogate != KIA_STE_WEIGHT && p->surrogate != KIA_STE_PROB) return KIA_ERR_PARAM;
+    if (p->grad_rule < KIA_GRAD_FULL || p->grad_rule > KIA_GRAD_MIN_ONLY) return KIA_ERR_PARAM;
+    if (p->calibration == KIA_CAL_FWM && !(p->tau > 0.f && isfinite(p->tau))) return KIA_ERR_PARAM;
+    return KIA_OK;
+}
+
+struct Shape {
+    int64_t B, H, T, d, BH, n_t, tiles_per_head;
+};
+
+kia_status check_shape(int B, int H, int T, int d, Shape* s) {
+    if (B < 1 || H < 1 || T < 1) return KIA_ERR_SHAPE;
+    if (d != 64 && d != 128) return KIA_ERR_SHAPE;
+    s->B = B; s->H = H; s->T = T; s->d = d;
+    s->BH = (int64_t)B * H;
+    s->n_t = ((int64_t)T + kia::kTile - 1) / kia::kTile;
+    s->tiles_per_head = s->n_t * (s->n_t + 1) / 2;
+    // grids are B*H*n_t workgroups; tensors and tile buffers are indexed in size_t
+    if (s->BH > INT32_MAX || s->BH * s->n_t > INT32_MAX) return KIA_ERR_SHAPE;
+    if ((double)s->BH * s->tiles_per_head * kia::kTileElems * 4.0 > 9.0e18) return KIA_ERR_SHAPE;
+    return KIA_OK;
+}
+
+bool prob_extras(const kia_params* p) {
+    return p->reconstruction == KIA_REC_NEAREST && p->surrogate == KIA_STE_PROB;
+}
+
+void stats_layout(const kia_params* p, const Shape& s, kia_stats_layout* L) {
+    size_t off = 0;
+    const size_t rows = (size_t)(s.BH * s.T);
+    L->scores = off;       off = align_up(off + (size_t)s.BH * s.tiles_per_head * kia::kTileElems * 4);
+    L->row_m = off;        off = align_up(off + rows * 4);
+    L->row_n = off;        off = align_up(off + rows * 4);
+    L->row_a = off;        off = align_up(off + rows * 4);
+    L->row_b = off;        off = align_up(off + rows * 4);
+    L->row_w = off;        off = align_up(off + rows * 4);
+    L->row_wl = off;       off = align_up(off + rows * 4);
+    if (prob_extras(p)) {
+        L->o_lerp = off;   off = align_up(off + rows * (size_t)s.d * 4);
+    } else {
+        L->o_lerp = 0;
+    }
+    L->total_bytes = off;
+    L->tiles_per_head = s.tiles_per_head;
+}
+
+void workspace_layout(const Shape& s, kia_workspace_layout* L) {
+    size_t off = 0;
+    const size_t rows = (size_t)(s.BH * s.T);
+    const size_t tiles = (size_t)s.BH * s.tiles_per_head * kia::kTileElems * 4;
+    L->probs = off;    off = align_up(off + tiles);
+    L->dscores = off;  off = align_up(off + tiles);
+    L->row_cm = off;   off = align_up(off + rows * 4);
+    L->row_cn = off;   off = align_up(off + rows * 4);
+    L->total_bytes = off;
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+kia_status record(const kia_ext* ext, int i, hipStream_t st) {
+    if (!ext || !ext->events || i >= ext->n_events || !ext->events[i]) return KIA_OK;
+    return hipEventRecord((hipEvent_t)ext->events[i], st) == hipSuccess ? KIA_OK : KIA_ERR_HIP;
+}
+
+kia::FwdConfig config_of(const kia_params* p, int d, bool dump) {
+    kia::FwdConfig c;
+    c.d = d;
+    c.cal = p->calibration;
+    c.rec = p->reconstruction;
+    c.prob = prob_extras(p);
+    c.dump = dump;
+    return c;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kia_stats_bytes(const kia_params* p, int B, int H, int T, int d) {
+    Shape s;
+    if (check_params(p) != KIA_OK || check_shape(B, H, T, d, &s) != KIA_OK) return 0;
+    kia_stats_layout L;
+    stats_layout(p, s, &L);
+    return L.total_bytes;
+}
+
+size_t kia_workspace_bytes(const kia_params* p, int B, int H, int T, int d) {
+    Shape s;
+    if (check_params(p) != KIA_OK || check_shape(B, H, T, d, &s) != KIA_OK) return 0;
+    kia_workspace_layout L;
+    workspace_layout(s, &L);
+    return L.total_bytes;
+}
+
+kia_status kia_stats_layout_query(const kia_params* p, int B, int H, int T, int d, kia_stats_layout* out) {
+    if (!out) return KIA_ERR_NULL;
+    kia_status st = check_params(p);
+    if (st != KIA_OK) return st;
+    Shape s;
+    if ((st = check_shape(B, H, T, d, &s)) != KIA_OK) return st;
+    stats_layout(p, s, out);
+    return KIA_OK;
+}
+
+kia_status kia_workspace_layout_query(const kia_params* p, int B, int H, int T, int d,
+                                      kia_workspace_layout* out) {
+    if (!out) return KIA_ERR_NULL;
+    kia_status st = check_params(p);
+    if (st != KIA_OK) return st;
+    Shape s;
+    if ((st = check_shape(B, H, T, d, &s)) != KIA_OK) return st;
+    workspace_layout(s, out);
+    return KIA_OK;
+}
+
+kia_status kia_forward_ext(const kia_params* p, int B, int H, int T, int d, const float* q, const float* k,
+                           const float* v, float* o, void* stats, size_t stats_bytes, void* stream,
+                           const kia_ext* ext) {
+    kia_status st = check_params(p);
+    if (st != KIA_OK) return st;
+    Shape s;
+    if ((st = check_shape(B, H, T, d, &s)) != KIA_OK) return st;
+    if (!q || !k || !v || !o || !stats) return KIA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(stats))
+        return KIA_ERR_ALIGN;
+    kia_stats_layout L;
+    stats_layout(p, s, &L);
+    if (stats_bytes < L.total_bytes) return KIA_ERR_BUFFER;
+    if (ext && ext->n_events < 0) return KIA_ERR_PARAM;
+
+    char* base = (char*)stats;
+    kia::FwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o;
+    a.tiles = (float*)(base + L.scores);
+    a.row_m = (float*)(base + L.row_m);
+    a.row_n = (float*)(base + L.row_n);
+    a.row_a = (int32_t*)(base + L.row_a);
+    a.row_b = (int32_t*)(base + L.row_b);
+    a.row_w = (float*)(base + L.row_w);
+    a.row_wl = (float*)(base + L.row_wl);
+    a.o_lerp = prob_extras(p) ? (float*)(base + L.o_lerp) : nullptr;
+    a.idx_dump = ext ? ext->idx_dump : nullptr;
+    a.BH = (int)s.BH; a.T = T; a.n_t = (int)s.n_t; a.K = p->n_intervals;
+    a.tau = p->tau;
+    a.scale = 1.f / sqrtf((float)d);
+
+    hipStream_t hs = (hipStream_t)stream;
+    if ((st = record(ext, 0, hs)) != KIA_OK) return st;
+    if (kia::launch_forward(config_of(p, d, a.idx_dump != nullptr), a, hs) != hipSuccess) return KIA_ERR_HIP;
+    return record(ext, 1, hs);
+}
+
+kia_status kia_forward(const kia_params* p, int B, int H, int T, int d, const float* q, const float* k,
+                       const float* v, float* o, void* stats, size_t stats_bytes, void* stream) {
+    return kia_forward_ext(p, B, H, T, d, q, k, v, o, stats, stats_bytes, stream, nullptr);
+}
+
+kia_status kia_backward_ext(const kia_params* p, int B, int H, int T, int d, const float* q, const float* k,
+                            const float* v, const float* o, const float* d_o, const void* stats,
+                            size_t stats_bytes, float* dq, float* dk, float* dv, void* ws, size_t ws_bytes,
+                            void* stream, const kia_ext* ext) {
+    kia_status st = check_params(p);
+    if (st != KIA_OK) return st;
+    Shape s;
+    if ((st = check_shape(B, H, T, d, &s)) != KIA_OK) return st;
+    if (!q || !k || !v || !o || !d_o || !stats || !dq || !dk || !dv || !ws) return KIA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(d_o) ||
+        !aligned16(stats) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(ws))
+        return KIA_ERR_ALIGN;
+    kia_stats_layout L;
+    stats_layout(p, s, &L);
+    if (stats_bytes < L.total_bytes) return KIA_ERR_BUFFER;
+    kia_workspace_layout WL;
+    workspace_layout(s, &WL);
+    if (ws_bytes < WL.total_bytes) return KIA_ERR_BUFFER;
+    if (ext && ext->n_events < 0) return KIA_ERR_PARAM;
+
+    const char* sb = (const char*)stats;
+    char* wb = (char*)ws;
+    kia::BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.d_o = d_o;
+    a.tiles = (const float*)(sb + L.scores);
+    a.row_m = (const float*)(sb + L.row_m);
+    a.row_n = (const float*)(sb + L.row_n);
+    a.row_a = (const int32_t*)(sb + L.row_a);
+    a.row_b = (const int32_t*)(sb + L.row_b);
+    a.row_w = (const float*)(sb + L.row_w);
+    a.row_wl = (const float*)(sb + L.row_wl);
+    a.o_lerp = prob_extras(p) ? (const float*)(sb + L.o_lerp) : nullptr;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.probs = (float*)(wb + WL.probs);
+    a.dscores = (float*)(wb + WL.dscores);
+    a.row_cm = (float*)(wb + WL.row_cm);
+    a.row_cn = (float*)(wb + WL.row_cn);
+    a.BH = (int)s.BH; a.T = T; a.n_t = (int)s.n_t; a.K = p->n_intervals;
+    a.tau = p->tau;
+    a.scale = 1.f / sqrtf((float)d);
+    a.rule = p->grad_rule;
+
+    hipStream_t hs = (hipStream_t)stream;
+    const kia::FwdConfig c = config_of(p, d, false);
+    if ((st = record(ext, 0, hs)) != KIA_OK) return st;
+    if (kia::launch_backward_rows(c, a, hs) != hipSuccess) return KIA_ERR_HIP;
+    if ((st = record(ext, 1, hs)) != KIA_OK) return st;
+    if ((st = record(ext, 2, hs)) != KIA_OK) return st;
+    if (kia::launch_backward_cols(d, a, hs) != hipSuccess) return KIA_ERR_HIP;
+    if ((st = record(ext, 3, hs)) != KIA_OK) return st;
+    if ((st = record(ext, 4, hs)) != KIA_OK) return st;
+    if (p->grad_rule != KIA_GRAD_DETACH && !(p->calibration == KIA_CAL_FWM && p->grad_rule == KIA_GRAD_MIN_ONLY)) {
+        if (kia::launch_backward_scatter(d, a, hs) != hipSuccess) return KIA_ERR_HIP;
+    }
+    return record(ext, 5, hs);
+}
+
+kia_status kia_backward(const kia_params* p, int B, int H, int T, int d, const float* q, const float* k,
+                        const float* v, const float* o, const float* d_o, const void* stats, size_t stats_bytes,
+                        float* dq, float* dk, float* dv, void* ws, size_t ws_bytes, void* stream) {
+    return kia_backward_ext(p, B, H, T, d, q, k, v, o, d_o, stats, stats_bytes, dq, dk, dv, ws, ws_bytes,
+                            stream, nullptr);
+}
+
+kia_status kia_tiles_to_dense(int B, int H, int T, const float* tiles, int key_major, float* dense,
+                              void* stream) {
+    if (!tiles || !dense) return KIA_ERR_NULL;
+    if (B < 1 || H < 1 || T < 1) return KIA_ERR_SHAPE;
+    if (key_major != 0 && key_major != 1) return KIA_ERR_PARAM;
+    const int64_t BH = (int64_t)B * H;
+    if (BH > 65535) return KIA_ERR_SHAPE;  // grid.y limit of the expansion kernel
+    const int64_t n_t = ((int64_t)T + 31) / 32;
+    if (n_t * (n_t + 1) / 2 > INT32_MAX) return KIA_ERR_SHAPE;
+    return kia::launch_tiles_to_dense((int)BH, T, tiles, key_major, dense, (hipStream_t)stream) == hipSuccess
+               ? KIA_OK
+               : KIA_ERR_HIP;
+}
+
+const char* kia_status_str(kia_status s) {
+    switch (s) {
+        case KIA_OK: return "ok";
+        case KIA_ERR_NULL: return "null pointer argument";
+        case KIA_ERR_SHAPE: return "unsupported shape (B, H, T >= 1; d in {64, 128})";
+        case KIA_ERR_PARAM: return "invalid operator parameter";
+        case KIA_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+        case KIA_ERR_BUFFER: return "stats or workspace buffer too small";
+        case KIA_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+int32_t kia_abi_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,238 @@
+"""GPU-vs-oracle comparison machinery for the parity tests.
+
+The HIP library is called through its C ABI (the ctypes binding); the oracle
+runs on the CPU in fp64 on the same fp32 inputs.  Nothing computed by the GPU
+is fed to the oracle.
+
+Decisions (LERP segment, Nearest grid point, FWM window edge, row argmax /
+argmin) are integers decided by floating point.  The kernel decides them on
+its fp32 scores, the oracle on fp64 scores, so a decision can legitimately
+differ when the oracle's u = (m - s)/h sits closer to a boundary than the two
+sides' u can differ.  That difference is bounded per pair by
+  |u_gpu_inputs - u_ref| + 4 * 2^-24 * (u_ref + 1)
+where u_gpu_inputs is (m - s)/h evaluated exactly on the GPU's own fp32
+scores and row max / min (its scores are first checked against the a-priori
+fp32 dot-product bound), and the second term covers the fp32 rounding of the
+kernel's subtraction, reciprocal and product.  Pairs inside twice that band
+are "ambiguous"; every comparison excludes exactly the outputs such a pair
+can move, and the tests report how many were excluded.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle as O
+
+TOL = 1e-4          # max error relative to the slice's max |reference| (fp32 path)
+ZERO_SUM_TOL = 1e-5
+
+
+def to_oracle_params(p):
+    cal = {"minmax": O.MINMAX, "fwm": O.FWM}[p.calibration]
+    rec = {"lerp": O.LERP, "nearest": O.NEAREST}[p.reconstruction]
+    ste = {"weight": O.WEIGHT_STE, "prob": O.PROB_STE}[p.surrogate]
+    rule = {"full": O.FULL, "detach": O.DETACH, "max_only": O.MAX_ONLY, "min_only": O.MIN_ONLY}[p.grad_rule]
+    return O.Params(K=p.K, tau=p.tau, calibration=cal, reconstruction=rec, surrogate=ste, grad_rule=rule)
+
+
+def run_gpu(q, k, v, do, params, want_dense=True, want_idx=True):
+    """Run kia_forward / kia_backward on cuda:0.  Returns a dict of device
+    tensors; SliceCheck copies out the (b, h) slices it needs."""
+    import torch
+    import quantized_softmax_attention_amd as kia
+
+    dev = torch.device("cuda:0")
+    tq, tk, tv, tdo = (torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (q, k, v, do))
+    B, H, T, d = q.shape
+    idx = None
+    if want_idx:
+        idx = torch.full((B, H, T, T), -7, dtype=torch.int32, device=dev)
+    o, stats = kia.kia_forward(tq, tk, tv, params, idx_dump=idx)
+    dq, dk, dv, ws = kia.kia_backward(tq, tk, tv, o, tdo, stats, params)
+    L = kia.kia_stats_layout_query(params, B, H, T, d)
+    WL = kia.kia_workspace_layout_query(params, B, H, T, d)
+    n = B * H * T
+
+    def rows(buf, off, dtype):
+        return buf[off: off + n * 4].view(dtype).reshape(B, H, T)
+
+    out = {
+        "O": o, "dQ": dq, "dK": dk, "dV": dv,
+        "m": rows(stats, L.row_m, torch.float32), "n": rows(stats, L.row_n, torch.float32),
+        "a": rows(stats, L.row_a, torch.int32), "b": rows(stats, L.row_b, torch.int32),
+        "W": rows(stats, L.row_w, torch.float32), "WL": rows(stats, L.row_wl, torch.float32),
+        "cm": rows(ws, WL.row_cm, torch.float32), "cn": rows(ws, WL.row_cn, torch.float32),
+        "_stats": stats, "_ws": ws,
+    }
+    if want_dense:
+        out["S"] = kia.kia_tiles_to_dense(B, H, T, stats[L.scores:], False)
+        out["P"] = kia.kia_tiles_to_dense(B, H, T, ws[WL.probs:], True)
+        out["dS"] = kia.kia_tiles_to_dense(B, H, T, ws[WL.dscores:], True)
+    if want_idx:
+        out["idx"] = idx
+    torch.cuda.synchronize()
+    return out
+
+
+def gpu_slice(gpu, b, h):
+    """numpy copies of every per-slice entry of a run_gpu result."""
+    return {key: val[b, h].cpu().numpy() for key, val in gpu.items() if not key.startswith("_")}
+
+
+def score_bound(Qh, Kh):
+    """A-priori bound on |fp32 score - exact score| per pair: a length-d fp32
+    dot product plus the scale multiply, (d + 2) * 2^-24 * sum_c |Q_c K_c| / sqrt(d)."""
+    d = Qh.shape[1]
+    absdot = np.abs(Qh.astype(np.float64)) @ np.abs(Kh.astype(np.float64)).T / np.sqrt(d)
+    return (d + 2) * 2.0 ** -24 * absdot
+
+
+class SliceCheck:
+    """Oracle for one (b, h) slice plus the ambiguity analysis against the GPU's run."""
+
+    def __init__(self, q, k, v, do, p_or, gpu, b, h):
+        self.p = p_or
+        Qh, Kh, Vh, dOh = q[b, h], k[b, h], v[b, h], do[b, h]
+        self.T, self.d = Qh.shape
+        self.ref = O.head_backward(Qh, Kh, Vh, dOh, p_or, keep_rows=True)
+        self.O_ref = np.stack([self.ref["rows"][t][0].P @ Vh[: t + 1].astype(np.float64)
+                               for t in range(self.T)])
+        self.g = gpu_slice(gpu, b, h)
+        self.sb = score_bound(Qh, Kh)
+        self._analyse()
+
+    def _analyse(self):
+        p, T, g = self.p, self.T, self.g
+        K = p.K
+        self.score_viol = 0
+        self.amb_fwd = np.zeros(T, dtype=bool)     # rows whose forward weights may differ
+        self.amb_bwd = np.zeros(T, dtype=bool)     # rows whose backward dS may differ
+        self.amb_keys_bwd = set()                  # keys whose dK may differ (LERP-continuous forward)
+        self.fwd_unstable_rows = []                # (t, max |dP| relative) for forward-ambiguous rows
+        self.n_amb_pairs = 0
+        self.idx_mismatch = 0
+        self.idx_checked = 0
+        for t in range(T):
+            fw, bw = self.ref["rows"][t]
+            s_ref = fw.s
+            cal = fw.cal
+            sg = g["S"][t, : t + 1].astype(np.float64) if "S" in g else None
+            if sg is not None:
+                viol = np.abs(sg - s_ref) > self.sb[t, : t + 1] * 1.0 + 1e-30
+                self.score_viol += int(viol.sum())
+            # argmax / argmin near ties
+            ds_obs = np.abs(sg - s_ref).max() if sg is not None else 0.0
+            tie_band = 2 * ds_obs + 4 * 2.0 ** -24 * (np.abs(s_ref).max() + 1)
+            srt = np.sort(s_ref)
+            ab_amb = False
+            if t >= 1:
+                if srt[-1] - srt[-2] <= tie_band:
+                    ab_amb = True
+                if p.calibration == O.MINMAX and srt[1] - srt[0] <= tie_band:
+                    ab_amb = True
+            if not ab_amb:
+                assert g["a"][t] == cal.a, (t, g["a"][t], cal.a)
+                if p.calibration == O.MINMAX:
+                    assert g["b"][t] == cal.b, (t, g["b"][t], cal.b)
+            if cal.degenerate or t == 0:
+                if ab_amb:
+                    self.amb_bwd[t] = True
+                continue
+            # decision band in grid steps
+            mg, ng = float(g["m"][t]), float(g["n"][t])
+            hg = (mg - ng) / K if p.calibration == O.MINMAX else p.tau / K
+            u_ref = fw.rec.u
+            u_pred = (mg - sg) / hg if sg is not None else u_ref
+            band = 2 * (np.abs(u_pred - u_ref) + 4 * 2.0 ** -24 * (np.abs(u_ref) + 1))
+            uc = np.minimum(u_ref, K)
+            knot = np.abs(uc - np.round(uc)) <= band                 # LERP segment boundaries
+            knot &= (uc > band) & (uc < K - band)                      # u = 0 / u = K are exact (max/min keys)
+            edge = (np.abs(u_ref - K) <= band) if p.calibration == O.FWM else np.zeros_like(knot)
+            half = np.abs(uc - (np.floor(uc) + 0.5)) <= band if p.reconstruction == O.NEAREST \
+                else np.zeros_like(knot)
+            fwd_amb = half | edge
+            bwd_amb = knot | fwd_amb
+            if ab_amb:
+                bwd_amb = bwd_amb | True
+            self.n_amb_pairs += int(bwd_amb.sum())
+            if fwd_amb.any():
+                # size of the possible weight jump relative to the row normaliser
+                jumps = []
+                for j in np.flatnonzero(fwd_amb):
+                    if edge[j]:
+                        jumps.append(fw.rec.g[K])
+                    else:
+                        r = int(np.floor(uc[j] + 0.5))
+                        lo, hi = max(r - 1, 0), min(r + 1, K)
+                        jumps.append(max(abs(fw.rec.g[r] - fw.rec.g[lo]), abs(fw.rec.g[hi] - fw.rec.g[r])))
+                rel = max(jumps) / fw.W
+                if rel > 1e-7:
+                    self.amb_fwd[t] = True
+                    self.fwd_unstable_rows.append((t, rel))
+            if bwd_amb.any():
+                self.amb_bwd[t] = True
+                self.amb_keys_bwd.update(int(j) for j in np.flatnonzero(bwd_amb))
+                self.amb_keys_bwd.add(int(cal.a))
+                self.amb_keys_bwd.add(int(cal.b))
+                if ab_amb:
+                    self.amb_keys_bwd.update(range(t + 1))
+            # grid index decisions, bit-exact away from boundaries
+            if "idx" in g:
+                gi = g["idx"][t, : t + 1]
+                if p.reconstruction == O.LERP:
+                    ri = np.where(fw.rec.mask > 0, fw.rec.i, -1)
+                    amb = knot | edge
+                else:
+                    ri = np.where(fw.rec.mask > 0, fw.rec.r, -1)
+                    amb = half | edge
+                ok = ~amb
+                self.idx_checked += int(ok.sum())
+                self.idx_mismatch += int((gi[ok] != ri[ok]).sum())
+
+    # ------------------------------------------------------------------
+    def compare(self, name, tol=TOL):
+        """Max error of an output relative to the slice's max |reference|,
+        over the entries no ambiguous decision can move."""
+        T = self.T
+        ref = {"O": self.O_ref, "dQ": self.ref["dQ"], "dK": self.ref["dK"], "dV": self.ref["dV"]}[name]
+        got = self.g[name].astype(np.float64)
+        keep = np.ones(T, dtype=bool)
+        if name == "O":
+            keep &= ~self.amb_fwd
+        elif name == "dQ":
+            keep &= ~(self.amb_fwd | self.amb_bwd)
+        elif name in ("dK", "dV"):
+            if name == "dK":
+                keep[list(self.amb_keys_bwd)] = False
+            for t, _ in self.fwd_unstable_rows:
+                keep[: t + 1] = False
+        scale = np.abs(ref).max()
+        if scale == 0:
+            return 0.0, int(keep.sum())
+        err = np.abs(got[keep] - ref[keep]).max() / scale if keep.any() else 0.0
+        return float(err), int(keep.sum())
+
+    def zero_sum_violations(self, q, k, v, do, b, h):
+        """Rows where |sum_j dS_tj| > 1e-5 * sum_j |dS_tj| on the GPU's own dS
+        (direct tiles plus the routed calibration terms at argmax / argmin).
+
+        The calibration terms make the row sum vanish for any dL/dw, so fp32
+        noise in dP and delta cancels there.  Degenerate-span rows have no
+        calibration terms: their sum is sum_j P_j dP_j - delta, which cancels
+        only to the rounding of two length-d fp32 dot products, so those rows
+        also get a floor of 4 d 2^-24 sum_j P_j sum_c |dO_c V_jc|."""
+        g = self.g
+        Vh, dOh = v[b, h].astype(np.float64), do[b, h].astype(np.float64)
+        bad = []
+        for t in range(self.T):
+            row = g["dS"][t, : t + 1].astype(np.float64).copy()
+            row[g["a"][t]] += g["cm"][t]
+            row[g["b"][t]] += g["cn"][t]
+            l1 = np.abs(row).sum()
+            floor = 0.0
+            fw = self.ref["rows"][t][0]
+            if fw.cal.degenerate:
+                floor = 4 * self.d * 2.0 ** -24 * float(fw.P @ (np.abs(Vh[: t + 1]) @ np.abs(dOh[t])))
+            if abs(row.sum()) > ZERO_SUM_TOL * l1 + floor:
+                bad.append((t, row.sum(), l1))
+        return bad

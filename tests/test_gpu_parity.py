@@ -1,0 +1,88 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bars (fp32 path): O, dQ, dK, dV within 1e-4 of the slice's max |reference|;
+grid indices (LERP segment / Nearest point) bit-exact away from boundaries;
+per-row |sum dS| <= 1e-5 * sum |dS| under the full rule; scores within the
+a-priori fp32 dot-product bound.  See tests/gpu_harness.py for how decisions
+near a boundary are excluded.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+from tests.gpu_harness import TOL, SliceCheck, run_gpu, to_oracle_params
+from workloads import WORKLOADS, Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def P(**kw):
+    from quantized_softmax_attention_amd import Params
+    return Params(**kw)
+
+
+def check(w: Workload, params, heads=None, max_amb_frac=0.02, verbose=True):
+    q, k, v, do = make_inputs(w)
+    print(f"[case] {w.name} B{w.B} H{w.H} T{w.T} d{w.d} {params}", flush=True)
+    g = run_gpu(q, k, v, do, params)
+    p_or = to_oracle_params(params)
+    heads = heads or [(b, h) for b in range(w.B) for h in range(w.H)]
+    worst = {}
+    n_amb = 0
+    for (b, h) in heads:
+        sc = SliceCheck(q, k, v, do, p_or, g, b, h)
+        assert sc.score_viol == 0, f"scores outside the fp32 bound in slice {(b, h)}"
+        assert sc.idx_mismatch == 0, f"{sc.idx_mismatch} grid indices differ in slice {(b, h)}"
+        for name in ("O", "dQ", "dK", "dV"):
+            err, kept = sc.compare(name)
+            worst[name] = max(worst.get(name, 0.0), err)
+            assert err <= TOL, f"{name} rel err {err:.3e} in slice {(b, h)} ({kept} rows compared)"
+        if params.grad_rule == "full":
+            bad = sc.zero_sum_violations(q, k, v, do, b, h)
+            assert not bad, f"zero-sum violated in slice {(b, h)}: {bad[:3]}"
+        n_amb += sc.n_amb_pairs
+    pairs = len(heads) * w.T * (w.T + 1) // 2
+    assert n_amb <= max_amb_frac * pairs
+    if verbose:
+        print(f"  worst rel err {worst}  ambiguous pairs {n_amb}/{pairs}", flush=True)
+    return g, worst
+
+
+SMALL = Workload("small_ragged", 2, 2, 80, 64, "scaled", q_scale=2.0)
+SMALL128 = Workload("small_ragged_d128", 1, 2, 75, 128, "head_temp", lo=0.5, hi=3.0)
+
+COMBOS = [("minmax", "lerp", "weight"), ("fwm", "lerp", "weight"),
+          ("minmax", "nearest", "weight"), ("minmax", "nearest", "prob"),
+          ("fwm", "nearest", "weight"), ("fwm", "nearest", "prob")]
+RULES = ["full", "detach", "max_only", "min_only"]
+
+
+@pytest.mark.parametrize("cal,rec,ste", COMBOS)
+@pytest.mark.parametrize("rule", RULES)
+def test_small_all_variants(cal, rec, ste, rule):
+    check(SMALL, P(K=4, tau=6.0, calibration=cal, reconstruction=rec, surrogate=ste, grad_rule=rule))
+
+
+@pytest.mark.parametrize("K", [1, 32, 64])
+@pytest.mark.parametrize("cal", ["minmax", "fwm"])
+def test_small_interval_counts(K, cal):
+    check(SMALL, P(K=K, tau=6.0, calibration=cal))
+
+
+@pytest.mark.parametrize("cal,rec,ste", COMBOS)
+def test_small_d128(cal, rec, ste):
+    check(SMALL128, P(K=16, tau=6.0, calibration=cal, reconstruction=rec, surrogate=ste))
+
+
+@pytest.mark.parametrize("T", [1, 2, 31, 32, 33, 64, 97])
+def test_edge_lengths(T):
+    w = Workload(f"len{T}", 1, 3, T, 64, "scaled", q_scale=2.0)
+    check(w, P(K=8))
+    check(w, P(K=4, calibration="fwm", reconstruction="nearest", surrogate="prob"))
+
+
+def test_c1_single_head_full_and_detach():
+    w = WORKLOADS["c1"]
+    for rule in ("full", "detach"):
+        check(w, P(K=32, calibration="minmax", reconstruction="lerp", grad_rule=rule))
