@@ -1,0 +1,286 @@
+"""Benchmark: K-interval attention forward + backward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload c2] [--variant ...]
+
+One step is one pass of the whole hot path over one batch: kia_forward then
+kia_backward (every kernel of both).  Inputs are synthetic (workloads/,
+seeded) and already resident in HBM when the timed region starts.  Prints
+ONE JSON line.  Throughput counts algorithmic work only: 12*d flop per causal
+(query, key) pair -- forward QK^T and PV, backward dP, dV, dQ, dK -- and not
+the masked upper triangle or any recomputation.
+
+Per-kernel times come from HIP events recorded by the library on the launch
+stream around each kernel inside the timed loop; the dominant kernel's
+algorithmic flops per launch over its mean duration is the roofline figure
+(fp32 matrix peak of the MI355X: 157.3 TFLOP/s).  Its HBM traffic is taken
+from the committed rocprofv3 counter summary when that summary was made from
+the current kernel sources, else reported as null.
+
+The CPU baseline times the fp64 oracle (tests' reference, not tuned) on a
+bounded sample of the same workload: a fixed number of (b, h) slices, one
+process per host core.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "K-interval attention fwd+bwd TFLOP/s and % MFMA roofline, GPT-2 124M shape"
+PEAK_FP32_MFMA = 157.3   # TFLOP/s, MI355X dense fp32 matrix
+PEAK_HBM = 8000.0        # GB/s
+CSRC = os.path.join(ROOT, "quantized_softmax_attention_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+# The headline variant per workload (the runs each workload is quoted on).
+DEFAULT_VARIANT = {
+    "c1": dict(K=32, calibration="minmax", reconstruction="lerp", surrogate="weight", grad_rule="full"),
+    "c2": dict(K=32, calibration="minmax", reconstruction="lerp", surrogate="weight", grad_rule="full"),
+    "c3": dict(K=4, calibration="fwm", reconstruction="nearest", surrogate="prob", grad_rule="full"),
+    "c4": dict(K=64, calibration="minmax", reconstruction="lerp", surrogate="weight", grad_rule="full"),
+    "c5": dict(K=64, calibration="minmax", reconstruction="lerp", surrogate="weight", grad_rule="full"),
+}
+KERNELS = ["forward", "backward_rows", "backward_cols"]
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them on the launch stream)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+
+    def make(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        self.events.extend(out)
+        return out
+
+    def ms(self, a, b):
+        t = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(t), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            return float("nan")
+        return float(t.value)
+
+    def close(self):
+        for e in self.events:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+        self.events = []
+
+
+def _oracle_slice(args):
+    """CPU-baseline worker: the oracle's forward+backward over one (b, h) slice."""
+    import numpy as np  # noqa: F401  (numpy imported with single-threaded BLAS)
+    import oracle as O
+    from workloads import WORKLOADS, make_inputs
+    wname, variant, b, h = args
+    q, k, v, do = _cached_inputs(wname)
+    cal = {"minmax": O.MINMAX, "fwm": O.FWM}[variant["calibration"]]
+    rec = {"lerp": O.LERP, "nearest": O.NEAREST}[variant["reconstruction"]]
+    ste = {"weight": O.WEIGHT_STE, "prob": O.PROB_STE}[variant["surrogate"]]
+    rule = {"full": O.FULL, "detach": O.DETACH, "max_only": O.MAX_ONLY, "min_only": O.MIN_ONLY}[variant["grad_rule"]]
+    p = O.Params(K=variant["K"], tau=6.0, calibration=cal, reconstruction=rec, surrogate=ste, grad_rule=rule)
+    t0 = time.perf_counter()
+    O.head_backward(q[b, h], k[b, h], v[b, h], do[b, h], p)   # runs the forward of every row too
+    return time.perf_counter() - t0
+
+
+_INPUTS = {}
+
+
+def _cached_inputs(wname):
+    from workloads import WORKLOADS, make_inputs
+    if wname not in _INPUTS:
+        _INPUTS[wname] = make_inputs(WORKLOADS[wname])
+    return _INPUTS[wname]
+
+
+def _pool_init():
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+
+
+def cpu_baseline(wname, variant, n_slices, flop_per_slice):
+    import multiprocessing as mp
+    from workloads import WORKLOADS
+    w = WORKLOADS[wname]
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16, n_slices))
+    slices = [(wname, variant, i // w.H % w.B, i % w.H) for i in range(n_slices)]
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(cores, initializer=_pool_init) as pool:
+        pool.map(_cached_inputs, [wname] * cores)           # input generation is not timed
+        t0 = time.perf_counter()
+        per = pool.map(_oracle_slice, slices)
+        wall = time.perf_counter() - t0
+    return {
+        "value": round(n_slices * flop_per_slice / wall / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"{n_slices} of {w.B * w.H} (b, h) slices of {wname} "
+                   f"(T={w.T}, d={w.d}), fp64 numpy forward+backward, one process per core; "
+                   f"{sum(per):.1f} s of CPU work in {wall:.1f} s wall"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2", choices=sorted(DEFAULT_VARIANT))
+    ap.add_argument("--K", type=int)
+    ap.add_argument("--calibration", choices=["minmax", "fwm"])
+    ap.add_argument("--reconstruction", choices=["lerp", "nearest"])
+    ap.add_argument("--surrogate", choices=["weight", "prob"])
+    ap.add_argument("--grad-rule", dest="grad_rule", choices=["full", "detach", "max_only", "min_only"])
+    ap.add_argument("--cpu-slices", type=int, default=32, help="oracle sample size for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB",
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: K-interval attention shards by (batch, head) slice with no "
+              "exchange, so a multi-GPU figure is the one-GPU figure times N; run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import quantized_softmax_attention_amd as kia
+    from workloads import WORKLOADS, make_inputs
+
+    dev = torch.device("cuda:0")
+    if args.copy_calib:
+        n = args.copy_calib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes_each_way": n * 4, "launches": 5}))
+        return
+
+    w = WORKLOADS[args.workload]
+    variant = dict(DEFAULT_VARIANT[args.workload])
+    for key in ("K", "calibration", "reconstruction", "surrogate", "grad_rule"):
+        if getattr(args, key) is not None:
+            variant[key] = getattr(args, key)
+    params = kia.Params(K=variant["K"], tau=6.0, calibration=variant["calibration"],
+                        reconstruction=variant["reconstruction"], surrogate=variant["surrogate"],
+                        grad_rule=variant["grad_rule"])
+
+    # the CPU baseline runs first, in child processes started before this
+    # process touches the GPU, and never overlaps the timed GPU region
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.workload, variant, args.cpu_slices, 12 * w.d * w.T * (w.T + 1) // 2)
+
+    q, k, v, do = make_inputs(w)
+    tq, tk, tv, tdo = (torch.from_numpy(x).to(dev) for x in (q, k, v, do))
+    B, H, T, d = q.shape
+    pairs = w.pairs()
+    flop_step = 12 * d * pairs
+    flop_kernel = 4 * d * pairs  # each of forward / backward_rows / backward_cols
+
+    o = torch.empty_like(tq)
+    stats = torch.empty(kia.kia_stats_bytes(params, B, H, T, d), dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(tq), torch.empty_like(tq), torch.empty_like(tq)
+    ws = torch.empty(kia.kia_workspace_bytes(params, B, H, T, d), dtype=torch.uint8, device=dev)
+
+    def step(evf=None, evb=None):
+        kia.kia_forward(tq, tk, tv, params, o=o, stats=stats, events=evf)
+        kia.kia_backward(tq, tk, tv, o, tdo, stats, params, dq=dq, dk=dk, dv=dv, ws=ws, events=evb)
+
+    for _ in range(args.warmup):
+        step()
+    ev = HipEvents()
+    evs = [(ev.make(2), ev.make(4)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for evf, evb in evs:
+        step(evf, evb)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ms_step = wall_ms / args.steps
+
+    per_kernel = {name: [] for name in KERNELS}
+    for evf, evb in evs:
+        per_kernel["forward"].append(ev.ms(evf[0], evf[1]))
+        per_kernel["backward_rows"].append(ev.ms(evb[0], evb[1]))
+        per_kernel["backward_cols"].append(ev.ms(evb[2], evb[3]))
+    ev.close()
+    kern_ms = {name: float(np.mean(vals)) for name, vals in per_kernel.items()}
+    dominant = max(("forward", "backward_rows", "backward_cols"), key=lambda n: kern_ms[n])
+    achieved = flop_kernel / (kern_ms[dominant] * 1e-3) / 1e12
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tr = json.load(open(TRAFFIC_FILE))
+            ent = tr.get("kernels", {}).get(dominant)
+            if ent and tr.get("source_digest") == source_digest() and tr.get("workload") == args.workload \
+                    and tr.get("variant") == variant:
+                traffic = ent["hbm_bytes_per_launch"]
+        except (ValueError, KeyError):
+            traffic = None
+
+    value = flop_step / (ms_step * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "T": T, "d": d, "causal": True,
+                   "K": variant["K"], "calibration": variant["calibration"],
+                   "reconstruction": variant["reconstruction"], "surrogate": variant["surrogate"],
+                   "grad_rule": variant["grad_rule"], "flop_per_step": flop_step},
+        "pct_mfma_roofline": round(100 * value / PEAK_FP32_MFMA, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP32_MFMA,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_MFMA, 4), "traffic": traffic,
+                     "kernel": dominant, "flop_per_launch": flop_kernel,
+                     "avg_ms": round(kern_ms[dominant], 4)},
+        "kernel_ms": {n: round(t, 4) for n, t in kern_ms.items()},
+    }
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

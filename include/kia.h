@@ -91,10 +91,10 @@ typedef struct kia_stats_layout {
 } kia_stats_layout;
 
 /* Byte offsets inside the backward workspace: the hard probabilities P and
- * the direct score gradient dS (calibration terms not included) as tiles in
- * key-major order (per (b, h): tile (qt, kt) at the same index as the score
- * tiles), and the per-row calibration terms actually routed by the gradient
- * rule to the argmax key (cm) and the argmin key (cn), fp32 [B*H*T]. */
+ * the score gradient dS (calibration terms included) as tiles in key-major
+ * order (per (b, h): tile (qt, kt) at the same index as the score tiles), and
+ * the per-row calibration terms the gradient rule routed to the argmax key
+ * (cm) and the argmin key (cn), fp32 [B*H*T]. */
 typedef struct kia_workspace_layout {
     size_t total_bytes;
     size_t probs;
@@ -131,7 +131,7 @@ kia_status kia_backward(const kia_params* p, int B, int H, int T, int d,
 
 /* Optional extras for the two calls above.  events: NULL or an array of
  * hipEvent_t (as void*) recorded on `stream` around each kernel: forward
- * uses 2 (start/end of its one kernel), backward 6 (around its three kernels,
+ * uses 2 (start/end of its one kernel), backward 4 (around its two kernels,
  * in launch order).  idx_dump (forward only): NULL or int32 [B,H,T,T]; for
  * every causal pair the kernel writes the grid index it used (the LERP
  * segment, or the Nearest grid point), -1 for keys outside the FWM window;

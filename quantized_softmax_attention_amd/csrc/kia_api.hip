@@ -227,12 +227,7 @@ kia_status kia_backward_ext(const kia_params* p, int B, int H, int T, int d, con
     if ((st = record(ext, 1, hs)) != KIA_OK) return st;
     if ((st = record(ext, 2, hs)) != KIA_OK) return st;
     if (kia::launch_backward_cols(d, a, hs) != hipSuccess) return KIA_ERR_HIP;
-    if ((st = record(ext, 3, hs)) != KIA_OK) return st;
-    if ((st = record(ext, 4, hs)) != KIA_OK) return st;
-    if (p->grad_rule != KIA_GRAD_DETACH && !(p->calibration == KIA_CAL_FWM && p->grad_rule == KIA_GRAD_MIN_ONLY)) {
-        if (kia::launch_backward_scatter(d, a, hs) != hipSuccess) return KIA_ERR_HIP;
-    }
-    return record(ext, 5, hs);
+    return record(ext, 3, hs);
 }
 
 kia_status kia_backward(const kia_params* p, int B, int H, int T, int d, const float* q, const float* k,

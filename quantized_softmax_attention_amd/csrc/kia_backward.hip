@@ -1,18 +1,19 @@
-// K-interval attention backward (gfx950): three kernels in stream order.
+// K-interval attention backward (gfx950): two kernels in stream order.
 //
-//   rows    one wavefront per (b, h, 32-query tile), sweeping the causal key
-//           tiles: reload the forward's scores, dP^T = V dO^T on the matrix
-//           cores, normalisation Jacobian at the surrogate's evaluation
-//           point, direct score gradient, running calibration sums; then
-//           dQ^T += K^T dS^T.  P and dS are written transposed (key-major) for
-//           the column kernel.  At the end of the row the calibration terms
-//           are complete: they are added to dQ (gathering K at the argmax and
-//           argmin keys) and stored per row.
-//   cols    one wavefront per (b, h, 32-key tile), sweeping the query tiles
-//           at or below the diagonal: dV^T += dO^T P and dK^T += Q^T dS.
-//   scatter per (b, h, 64-key block): adds the calibration terms of every row
-//           whose argmax / argmin key is in the block, C * Q_t / sqrt(d), to
-//           dK in row order (deterministic, no atomics).
+//   rows  a workgroup (4 wavefronts) owns 128 queries of one (b, h) slice and
+//         sweeps the causal key tiles, V and K^T staged in LDS per tile
+//         (double-buffered).  Per tile: reload the forward's scores,
+//         dP^T = V dO^T on the matrix cores, normalisation Jacobian at the
+//         surrogate's evaluation point, direct score gradient, running
+//         calibration sums, dQ^T += K^T dS^T; P and dS are written key-major
+//         for the column kernel.  At the end of the row the calibration terms
+//         are complete: they are added to dQ (gathering K at the argmax and
+//         argmin keys) and folded into the wave's own dS tiles at (t, argmax)
+//         and (t, argmin), so the column kernel's dK contraction carries them.
+//   cols  a workgroup owns 128 keys and sweeps the query tiles at or below
+//         the diagonal, dO^T and Q^T staged in LDS: dV^T += dO^T P and
+//         dK^T += Q^T dS.
+// No atomics: every output element has one writer and a fixed summation order.
 //
 // Gradient rules: "Pretraining Transformers with Quantized Softmax in
 // Attention" (paperlayer digest), section 3 "Calibration gradients" and
@@ -28,58 +29,43 @@
 //            with Wd_j = dw/du * (-u/h) + dw/dh|_u = g ((c/h - 1) u + f (i+1) c)
 //   FWM      C_m = sum_j dL/dw_j dw/du / h,  C_n = 0 (h does not depend on the row)
 //   full adds C_m at the argmax and C_n at the argmin; detach adds neither;
-//   max-only / min-only add one.  Degenerate rows: dS = P (dP - delta), no C.
+//   max-only / min-only add one.  Degenerate rows: dS = P (dP - delta), no C;
+//   a row with a single causal key has P = 1 identically and dS = 0.
 #include "kia_common.hpp"
 #include "kia_kernels.hpp"
 
 namespace kia {
 
-__device__ __forceinline__ void map_rows_task_b(int g, int BH, int n_t, int& bh, int& qt) {
-    if ((BH & 7) == 0) {
-        const int x = g & 7, s = g >> 3, per = BH >> 3;
-        qt = n_t - 1 - s / per;
-        bh = (s % per) * 8 + x;
-    } else {
-        qt = n_t - 1 - g / BH;
-        bh = g % BH;
-    }
-}
-
-// Key-stationary mapping: the first key tiles see the most query tiles.
-__device__ __forceinline__ void map_cols_task(int g, int BH, int n_t, int& bh, int& kt) {
-    if ((BH & 7) == 0) {
-        const int x = g & 7, s = g >> 3, per = BH >> 3;
-        kt = s / per;
-        bh = (s % per) * 8 + x;
-    } else {
-        kt = g / BH;
-        bh = g % BH;
-    }
-}
-
 template <int D, int CAL, int REC, bool PROB>
-__global__ __launch_bounds__(64) void kia_backward_rows_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows_kernel(BwdArgs a) {
     constexpr int NB = D / 32;
-    constexpr int LDS_STRIDE = kTile + 1;
-    __shared__ float lds_p[kTile * LDS_STRIDE];
-    __shared__ float lds_ds[kTile * LDS_STRIDE];
+    using ST = StreamTile<D>;
+    constexpr int BUF = ST::kRM + ST::kTR;  // V row-major, then K transposed
+    constexpr int XS = 36;                  // row stride of the per-wave transpose scratch
+    __shared__ __attribute__((aligned(16))) float lds[2 * BUF];
+    __shared__ __attribute__((aligned(16))) float xpose[kWaves * kTile * XS];
 
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
     const int li = lane & 31, hl = lane >> 5;
-    int bh, qt;
-    map_rows_task_b(blockIdx.x, a.BH, a.n_t, bh, qt);
-    const int T = a.T;
-    const int q0 = qt * kTile;
-    const int qrow = q0 + li;
-    const bool qvalid = qrow < T;
+    const int T = a.T, n_t = a.n_t;
+    const int n_blk = (n_t + kBlockTiles - 1) / kBlockTiles;
+    int bh, blk;
+    map_block(blockIdx.x, a.BH, n_blk, true, bh, blk);
+    const int qt = blk * kBlockTiles + wave;
+    const bool active = qt < n_t;
+    const int kt_end = min(blk * kBlockTiles + kBlockTiles - 1, n_t - 1);
+    const int qrow = qt * kTile + li;
+    const bool qvalid = active && qrow < T;
     const size_t head = (size_t)bh * T * D;
     const float* Kp = a.k + head;
     const float* V = a.v + head;
-    const int64_t tiles_per_head = (int64_t)a.n_t * (a.n_t + 1) / 2;
-    const size_t tile0 = ((size_t)bh * tiles_per_head + tile_index(qt, 0)) * kTileElems;
+    const int64_t tiles_per_head = (int64_t)n_t * (n_t + 1) / 2;
+    const size_t tile0 = ((size_t)bh * tiles_per_head + (active ? tile_index(qt, 0) : 0)) * kTileElems;
     const float* stiles = a.tiles + tile0;
     float* ptiles = a.probs + tile0;
     float* dstiles = a.dscores + tile0;
+    float* xw = xpose + wave * kTile * XS;
 
     // B operand of dP^T = V dO^T (dO row of this lane's query), and delta.
     const float* oe = (REC == REC_NEAREST && PROB) ? a.o_lerp : a.o;
@@ -115,85 +101,98 @@ __global__ __launch_bounds__(64) void kia_backward_rows_kernel(BwdArgs a) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) dq[b] = f32x16{};
 
-    for (int kt = 0; kt <= qt; ++kt) {
-        const int k0 = kt * kTile;
-        const int krow = k0 + li;
-        float sv[16];
-        {
-            const float* tp = stiles + (size_t)kt * kTileElems;
+    ST sv_, sk_;
+    sv_.load_rm(V, 0, T, tid);
+    sk_.load_tr(Kp, 0, T, tid);
+    sv_.store_rm(lds, tid);
+    sk_.store_tr(lds + ST::kRM, tid);
+    f32x4 snext[4];
+    if (active) {
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                f32x4 x = *(const f32x4*)(tp + p * 256 + lane * 4);
+        for (int p = 0; p < 4; ++p) snext[p] = *(const f32x4*)(stiles + p * 256 + lane * 4);
+    }
+    __syncthreads();
+
+    for (int kt = 0; kt <= kt_end; ++kt) {
+        const float* vcur = lds + (kt & 1) * BUF;
+        const float* kcur = vcur + ST::kRM;
+        if (kt < kt_end) {
+            sv_.load_rm(V, (kt + 1) * kTile, T, tid);
+            sk_.load_tr(Kp, (kt + 1) * kTile, T, tid);
+        }
+        if (active && kt <= qt) {
+            const int k0 = kt * kTile;
+            float sv[16];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) sv[4 * p + j] = x[j];
+            for (int p = 0; p < 4; ++p)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sv[4 * p + j] = snext[p][j];
+            if (kt < qt) {
+                const float* tp = stiles + (size_t)(kt + 1) * kTileElems;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) snext[p] = *(const f32x4*)(tp + p * 256 + lane * 4);
             }
-        }
-        // dP^T = V dO^T : A operand row = key
-        float vf[D / 2];
+            // dP^T = V dO^T : A operand row = key
+            f32x16 dp = {};
 #pragma unroll
-        for (int p = 0; p < D / 8; ++p) {
-            f32x4 x = {0.f, 0.f, 0.f, 0.f};
-            if (krow < T) x = *(const f32x4*)(V + (size_t)krow * D + 8 * p + 4 * hl);
+            for (int p = 0; p < D / 8; ++p) {
+                const f32x4 x = *(const f32x4*)(vcur + rm_off<D>(li, 8 * p + 4 * hl));
 #pragma unroll
-            for (int j = 0; j < 4; ++j) vf[4 * p + j] = x[j];
-        }
-        f32x16 dp = {};
-#pragma unroll
-        for (int kk = 0; kk < D / 2; ++kk) dp = mfma32x32x2(vf[kk], dof[kk], dp);
+                for (int j = 0; j < 4; ++j) dp = mfma32x32x2(x[j], dof[4 * p + j], dp);
+            }
 
-        float ds[16], pr[16];
+            float ds[16], pr[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = k0 + acc_row(r, hl);
-            const bool valid = qvalid && key <= qrow;
-            const Recon e = reconstruct<CAL, REC == REC_NEAREST>(rg, sv[r]);
-            const bool keep = valid && e.inwin;
-            const float wh = (REC == REC_LERP) ? e.wl : e.wn;
-            pr[r] = keep ? wh * invW : 0.f;
-            const float gt = (dp[r] - dlt) * invWe;
-            const float A = gt * e.g * rg.coh;
-            const float Wd = e.g * fmaf(rg.coh - 1.f, e.uc, e.f * (e.fi + 1.f) * rg.c);
-            ds[r] = keep ? A : 0.f;
-            SA += ds[r];
-            SB += keep ? gt * Wd : 0.f;
-        }
+            for (int r = 0; r < 16; ++r) {
+                const int key = k0 + acc_row(r, hl);
+                const bool valid = qvalid && key <= qrow;
+                const Recon e = reconstruct<CAL, REC == REC_NEAREST>(rg, sv[r]);
+                const bool keep = valid && e.inwin;
+                const float wh = (REC == REC_LERP) ? e.wl : e.wn;
+                pr[r] = keep ? wh * invW : 0.f;
+                const float gt = (dp[r] - dlt) * invWe;
+                const float A = gt * e.g * rg.coh;
+                const float Wd = e.g * fmaf(rg.coh - 1.f, e.uc, e.f * (e.fi + 1.f) * rg.c);
+                ds[r] = keep ? A : 0.f;
+                SA += ds[r];
+                SB += keep ? gt * Wd : 0.f;
+            }
 
-        // transpose P and dS to key-major through LDS
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int kj = acc_row(r, hl);
-            lds_p[kj * LDS_STRIDE + li] = pr[r];
-            lds_ds[kj * LDS_STRIDE + li] = ds[r];
-        }
-        __syncthreads();
-        {
+            // P and dS to key-major tiles through the wave's LDS scratch
             float* pp = ptiles + (size_t)kt * kTileElems;
             float* dd = dstiles + (size_t)kt * kTileElems;
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                f32x4 x, y;
+            for (int r = 0; r < 16; ++r) xw[acc_row(r, hl) * XS + li] = pr[r];
+            __builtin_amdgcn_wave_barrier();
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int qq = 2 * (4 * p + j) + hl;
-                    x[j] = lds_p[li * LDS_STRIDE + qq];
-                    y[j] = lds_ds[li * LDS_STRIDE + qq];
+            for (int p = 0; p < 4; ++p)
+                *(f32x4*)(pp + p * 256 + lane * 4) = *(const f32x4*)(xw + li * XS + 8 * p + 4 * hl);
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int r = 0; r < 16; ++r) xw[acc_row(r, hl) * XS + li] = ds[r];
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                *(f32x4*)(dd + p * 256 + lane * 4) = *(const f32x4*)(xw + li * XS + 8 * p + 4 * hl);
+            __builtin_amdgcn_wave_barrier();
+
+            // dQ^T += K^T dS^T : A operand row = head-dim index
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const f32x4 x = *(const f32x4*)(kcur + tr_off(32 * b + li, 8 * p + 4 * hl));
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) dq[b] = mfma32x32x2(x[j], ds[4 * p + j], dq[b]);
                 }
-                *(f32x4*)(pp + p * 256 + lane * 4) = x;
-                *(f32x4*)(dd + p * 256 + lane * 4) = y;
             }
+        }
+        if (kt < kt_end) {
+            float* nxt = lds + ((kt + 1) & 1) * BUF;
+            sv_.store_rm(nxt, tid);
+            sk_.store_tr(nxt + ST::kRM, tid);
         }
         __syncthreads();
-
-        // dQ^T += K^T dS^T
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-#pragma unroll
-            for (int kk = 0; kk < 16; ++kk) {
-                const int key = k0 + acc_row(kk, hl);
-                const float kv = key < T ? Kp[(size_t)key * D + 32 * b + li] : 0.f;
-                dq[b] = mfma32x32x2(kv, ds[kk], dq[b]);
-            }
-        }
     }
 
     SA += __shfl_xor(SA, 32);
@@ -212,6 +211,8 @@ __global__ __launch_bounds__(64) void kia_backward_rows_kernel(BwdArgs a) {
     const float cm = use_max ? Cm : 0.f;
     const float cn = use_min ? Cn : 0.f;
 
+    // the wave's dS tile stores must be visible before it updates two entries per row
+    __threadfence_block();
     if (qvalid) {
         const int ka = a.row_a[ri];
         const int kb = a.row_b[ri];
@@ -225,61 +226,113 @@ __global__ __launch_bounds__(64) void kia_backward_rows_kernel(BwdArgs a) {
                 const f32x4 xb = *(const f32x4*)(Kp + (size_t)kb * D + c);
                 f32x4 y;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    y[j] = (dq[b][4 * p + j] + cm * xa[j] + cn * xb[j]) * a.scale;
+                for (int j = 0; j < 4; ++j) y[j] = (dq[b][4 * p + j] + cm * xa[j] + cn * xb[j]) * a.scale;
                 *(f32x4*)(dqrow + c) = y;
             }
         if (hl == 0) {
             a.row_cm[ri] = cm;
             a.row_cn[ri] = cn;
+            // fold the routed calibration terms into the row's dS (argmax != argmin
+            // whenever they are non-zero, so the two updates never meet)
+            if (cm != 0.f) {
+                float* e = dstiles + (size_t)(ka >> 5) * kTileElems + kmajor_offset(li, ka & 31);
+                *e += cm;
+            }
+            if (cn != 0.f) {
+                float* e = dstiles + (size_t)(kb >> 5) * kTileElems + kmajor_offset(li, kb & 31);
+                *e += cn;
+            }
         }
     }
 }
 
 template <int D>
-__global__ __launch_bounds__(64) void kia_backward_cols_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_cols_kernel(BwdArgs a) {
     constexpr int NB = D / 32;
-    const int lane = threadIdx.x;
+    using ST = StreamTile<D>;
+    constexpr int BUF = 2 * ST::kTR;  // dO^T, then Q^T
+    __shared__ __attribute__((aligned(16))) float lds[2 * BUF];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
     const int li = lane & 31, hl = lane >> 5;
-    int bh, kt;
-    map_cols_task(blockIdx.x, a.BH, a.n_t, bh, kt);
-    const int T = a.T;
+    const int T = a.T, n_t = a.n_t;
+    const int n_blk = (n_t + kBlockTiles - 1) / kBlockTiles;
+    int bh, blk;
+    map_block(blockIdx.x, a.BH, n_blk, false, bh, blk);
+    const int kt = blk * kBlockTiles + wave;
+    const bool active = kt < n_t;
+    const int qt_begin = blk * kBlockTiles;
     const int krow = kt * kTile + li;
     const size_t head = (size_t)bh * T * D;
     const float* Q = a.q + head;
     const float* dO = a.d_o + head;
-    const int64_t tiles_per_head = (int64_t)a.n_t * (a.n_t + 1) / 2;
+    const int64_t tiles_per_head = (int64_t)n_t * (n_t + 1) / 2;
     const size_t hbase = (size_t)bh * tiles_per_head;
 
     f32x16 dv[NB], dk[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) { dv[b] = f32x16{}; dk[b] = f32x16{}; }
 
-    for (int qt = kt; qt < a.n_t; ++qt) {
-        const size_t toff = (hbase + tile_index(qt, kt)) * kTileElems;
-        float pv[16], dsv[16];
+    ST so_, sq_;
+    so_.load_tr(dO, qt_begin * kTile, T, tid);
+    sq_.load_tr(Q, qt_begin * kTile, T, tid);
+    so_.store_tr(lds, tid);
+    sq_.store_tr(lds + ST::kTR, tid);
+    f32x4 pnext[4], dnext[4];
+    if (active) {
+        const size_t toff = (hbase + tile_index(kt, kt)) * kTileElems;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const f32x4 x = *(const f32x4*)(a.probs + toff + p * 256 + lane * 4);
-            const f32x4 y = *(const f32x4*)(a.dscores + toff + p * 256 + lane * 4);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) { pv[4 * p + j] = x[j]; dsv[4 * p + j] = y[j]; }
-        }
-        const int q0 = qt * kTile;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-#pragma unroll
-            for (int kk = 0; kk < 16; ++kk) {
-                const int q = q0 + 2 * kk + hl;
-                const bool ok = q < T;
-                const float dov = ok ? dO[(size_t)q * D + 32 * b + li] : 0.f;
-                const float qv = ok ? Q[(size_t)q * D + 32 * b + li] : 0.f;
-                dv[b] = mfma32x32x2(dov, pv[kk], dv[b]);
-                dk[b] = mfma32x32x2(qv, dsv[kk], dk[b]);
-            }
+            pnext[p] = *(const f32x4*)(a.probs + toff + p * 256 + lane * 4);
+            dnext[p] = *(const f32x4*)(a.dscores + toff + p * 256 + lane * 4);
         }
     }
-    if (krow < T) {
+    __syncthreads();
+
+    for (int qt = qt_begin; qt < n_t; ++qt) {
+        const float* ocur = lds + (qt & 1) * BUF;
+        const float* qcur = ocur + ST::kTR;
+        if (qt + 1 < n_t) {
+            so_.load_tr(dO, (qt + 1) * kTile, T, tid);
+            sq_.load_tr(Q, (qt + 1) * kTile, T, tid);
+        }
+        if (active && qt >= kt) {
+            float pv[16], dsv[16];
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) { pv[4 * p + j] = pnext[p][j]; dsv[4 * p + j] = dnext[p][j]; }
+            if (qt + 1 < n_t) {
+                const size_t toff = (hbase + tile_index(qt + 1, kt)) * kTileElems;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    pnext[p] = *(const f32x4*)(a.probs + toff + p * 256 + lane * 4);
+                    dnext[p] = *(const f32x4*)(a.dscores + toff + p * 256 + lane * 4);
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const f32x4 x = *(const f32x4*)(ocur + tr_off(32 * b + li, 8 * p + 4 * hl));
+                    const f32x4 y = *(const f32x4*)(qcur + tr_off(32 * b + li, 8 * p + 4 * hl));
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        dv[b] = mfma32x32x2(x[j], pv[4 * p + j], dv[b]);
+                        dk[b] = mfma32x32x2(y[j], dsv[4 * p + j], dk[b]);
+                    }
+                }
+            }
+        }
+        if (qt + 1 < n_t) {
+            float* nxt = lds + ((qt + 1) & 1) * BUF;
+            so_.store_tr(nxt, tid);
+            sq_.store_tr(nxt + ST::kTR, tid);
+        }
+        __syncthreads();
+    }
+    if (active && krow < T) {
         float* dkrow = a.dk + head + (size_t)krow * D;
         float* dvrow = a.dv + head + (size_t)krow * D;
 #pragma unroll
@@ -287,77 +340,18 @@ __global__ __launch_bounds__(64) void kia_backward_cols_kernel(BwdArgs a) {
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 const int c = 32 * b + 8 * p + 4 * hl;
-                f32x4 x, y;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    x[j] = dk[b][4 * p + j] * a.scale;
-                    y[j] = dv[b][4 * p + j];
-                }
-                *(f32x4*)(dkrow + c) = x;
-                *(f32x4*)(dvrow + c) = y;
+                *(f32x4*)(dkrow + c) = f32x4{dk[b][4 * p] * a.scale, dk[b][4 * p + 1] * a.scale,
+                                             dk[b][4 * p + 2] * a.scale, dk[b][4 * p + 3] * a.scale};
+                *(f32x4*)(dvrow + c) = f32x4{dv[b][4 * p], dv[b][4 * p + 1], dv[b][4 * p + 2], dv[b][4 * p + 3]};
             }
-    }
-}
-
-// Calibration terms onto dK: block of 64 keys, rows in ascending order.
-template <int D>
-__global__ __launch_bounds__(64) void kia_backward_scatter_kernel(BwdArgs a) {
-    constexpr int KB = 64;
-    __shared__ float acc[KB * D];
-    const int lane = threadIdx.x;
-    const int T = a.T;
-    const int nkb = (T + KB - 1) / KB;
-    const int bh = blockIdx.x / nkb;
-    const int j0 = (blockIdx.x % nkb) * KB;
-    const size_t head = (size_t)bh * T * D;
-    const float* Q = a.q + head;
-    for (int i = lane; i < KB * D; i += kWave) acc[i] = 0.f;
-    __syncthreads();
-    bool any = false;
-    for (int t0 = j0; t0 < T; t0 += kWave) {
-        const int t = t0 + lane;
-        int ta = -1, tb = -1;
-        float cm = 0.f, cn = 0.f;
-        if (t < T) {
-            const size_t ri = (size_t)bh * T + t;
-            ta = a.row_a[ri];
-            tb = a.row_b[ri];
-            cm = a.row_cm[ri];
-            cn = a.row_cn[ri];
-        }
-        const bool hit_a = cm != 0.f && ta >= j0 && ta < j0 + KB;
-        const bool hit_b = cn != 0.f && tb >= j0 && tb < j0 + KB;
-        unsigned long long bal = __ballot(hit_a || hit_b);
-        while (bal) {
-            const int src = __ffsll(bal) - 1;
-            bal &= bal - 1;
-            const int ts = t0 + src;
-            const int as = __shfl(ta, src), bs = __shfl(tb, src);
-            const float cms = __shfl(cm, src), cns = __shfl(cn, src);
-            const bool ha = __shfl((int)hit_a, src) != 0;
-            const bool hb = __shfl((int)hit_b, src) != 0;
-            for (int c = lane; c < D; c += kWave) {
-                const float qv = Q[(size_t)ts * D + c];
-                if (ha) acc[(as - j0) * D + c] += cms * qv;
-                if (hb) acc[(bs - j0) * D + c] += cns * qv;
-            }
-            any = true;
-        }
-    }
-    if (!any) return;  // uniform across the wave (the ballot is)
-    __syncthreads();
-    for (int j = 0; j < KB; ++j) {
-        const int key = j0 + j;
-        if (key >= T) break;
-        float* dkrow = a.dk + head + (size_t)key * D;
-        for (int c = lane; c < D; c += kWave) dkrow[c] += acc[j * D + c] * a.scale;
     }
 }
 
 template <int D, int CAL, int REC, bool PROB>
 static hipError_t launch_rows_t(const BwdArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((kia_backward_rows_kernel<D, CAL, REC, PROB>), dim3((unsigned)(a.BH * a.n_t)),
-                       dim3(kWave), 0, s, a);
+    const int n_blk = (a.n_t + kBlockTiles - 1) / kBlockTiles;
+    hipLaunchKernelGGL((kia_backward_rows_kernel<D, CAL, REC, PROB>), dim3((unsigned)(a.BH * n_blk)),
+                       dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -378,20 +372,12 @@ hipError_t launch_backward_rows(const FwdConfig& c, const BwdArgs& a, hipStream_
 }
 
 hipError_t launch_backward_cols(int d, const BwdArgs& a, hipStream_t s) {
-    const dim3 grid((unsigned)(a.BH * a.n_t));
+    const int n_blk = (a.n_t + kBlockTiles - 1) / kBlockTiles;
+    const dim3 grid((unsigned)(a.BH * n_blk));
     if (d == 64)
-        hipLaunchKernelGGL((kia_backward_cols_kernel<64>), grid, dim3(kWave), 0, s, a);
+        hipLaunchKernelGGL((kia_backward_cols_kernel<64>), grid, dim3(kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((kia_backward_cols_kernel<128>), grid, dim3(kWave), 0, s, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_backward_scatter(int d, const BwdArgs& a, hipStream_t s) {
-    const dim3 grid((unsigned)((a.T + 63) / 64 * a.BH));
-    if (d == 64)
-        hipLaunchKernelGGL((kia_backward_scatter_kernel<64>), grid, dim3(kWave), 0, s, a);
-    else
-        hipLaunchKernelGGL((kia_backward_scatter_kernel<128>), grid, dim3(kWave), 0, s, a);
+        hipLaunchKernelGGL((kia_backward_cols_kernel<128>), grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

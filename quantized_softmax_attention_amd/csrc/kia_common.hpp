@@ -55,12 +55,84 @@ __host__ __device__ __forceinline__ int qmajor_offset(int qi, int kj) {
     return (kj >> 3) * 256 + (qi + 32 * ((kj >> 2) & 1)) * 4 + (kj & 3);
 }
 
-// Key-major tile storage used for P and dS in the backward: lane l (key
-// l%32, half h) holds queries 2*kk + h at register kk, stored as float4
-// (kk/4) at (kk/4)*256 + 4*l.  Element (query qi, key kj): lane
-// kj + 32*(qi&1), register qi>>1.
-__host__ __device__ __forceinline__ int kmajor_offset(int qi, int kj) {
-    return ((qi >> 1) >> 2) * 256 + (kj + 32 * (qi & 1)) * 4 + ((qi >> 1) & 3);
+// Key-major tile storage used for P and dS in the backward: the same
+// arrangement with the roles of query and key swapped, so lane l holds key
+// l%32 and its registers walk the queries 8*(r/4) + 4*(l/32) + r%4.
+__host__ __device__ __forceinline__ int kmajor_offset(int qi, int kj) { return qmajor_offset(kj, qi); }
+
+// ---- workgroup tiling --------------------------------------------------------
+// A workgroup of 4 wavefronts owns 128 stationary rows (32 per wave) and
+// streams 32-row tiles of the other operand through LDS, double-buffered.
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kBlockTiles = kWaves;  // stationary 32-row tiles per workgroup
+
+// LDS layouts of a streamed 32 x D tile (rows r of a row-major [T][D] tensor):
+//  row-major  rm(r, c) = r*(D+4) + c: lane = row, float4 along c (no conflicts)
+//  transposed tr(c, r) = c*32 + 4*((r/4) ^ (c%8)) + r%4: lane = column c,
+//             float4 along 4 consecutive rows; the xor spreads both the
+//             staging writes and the float4 reads over all banks.
+template <int D>
+__device__ __forceinline__ int rm_off(int r, int c) { return r * (D + 4) + c; }
+__device__ __forceinline__ int tr_off(int c, int r) { return c * kTile + 4 * ((r >> 2) ^ (c & 7)) + (r & 3); }
+
+template <int D>
+struct StreamTile {
+    static constexpr int kF4 = kTile * D / 4 / kThreads;  // float4 per thread
+    static constexpr int kRM = kTile * (D + 4);          // floats of a row-major staged tile
+    static constexpr int kTR = D * kTile;                // floats of a transposed staged tile
+    f32x4 v[kF4];
+
+    // row-major staging: consecutive threads read consecutive float4 of a row
+    __device__ __forceinline__ void load_rm(const float* src, int r0, int T, int tid) {
+#pragma unroll
+        for (int i = 0; i < kF4; ++i) {
+            const int e = tid + kThreads * i, r = e / (D / 4), c4 = e % (D / 4);
+            v[i] = (r0 + r < T) ? *(const f32x4*)(src + (size_t)(r0 + r) * D + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    __device__ __forceinline__ void store_rm(float* lds, int tid) const {
+#pragma unroll
+        for (int i = 0; i < kF4; ++i) {
+            const int e = tid + kThreads * i, r = e / (D / 4), c4 = e % (D / 4);
+            *(f32x4*)(lds + rm_off<D>(r, 4 * c4)) = v[i];
+        }
+    }
+    // transposed staging: a wave's lanes take 32 consecutive rows of one float4 column
+    __device__ __forceinline__ void load_tr(const float* src, int r0, int T, int tid) {
+#pragma unroll
+        for (int i = 0; i < kF4; ++i) {
+            const int e = tid + kThreads * i, r = e & 31, c4 = e >> 5;
+            v[i] = (r0 + r < T) ? *(const f32x4*)(src + (size_t)(r0 + r) * D + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    __device__ __forceinline__ void store_tr(float* lds, int tid) const {
+#pragma unroll
+        for (int i = 0; i < kF4; ++i) {
+            const int e = tid + kThreads * i, r = e & 31, c4 = e >> 5;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) lds[tr_off(4 * c4 + j, r)] = v[i][j];
+        }
+    }
+};
+
+// Heaviest-first work order over (slice, 128-row block) pairs.  Blocks of one
+// slice share K and V; workgroups are dealt round-robin to the 8 XCDs, so when
+// B*H is a multiple of 8 all blocks of a slice are kept on one XCD (one L2).
+// `descending` puts high block indices first (query-stationary kernels: the
+// last query blocks see the most keys); otherwise low indices first.
+__device__ __forceinline__ void map_block(int g, int BH, int nb, bool descending, int& bh, int& blk) {
+    int s;
+    if ((BH & 7) == 0) {
+        const int x = g & 7, per = BH >> 3;
+        s = g >> 3;
+        bh = (s % per) * 8 + x;
+        blk = s / per;
+    } else {
+        bh = g % BH;
+        blk = g / BH;
+    }
+    if (descending) blk = nb - 1 - blk;
 }
 
 // Per-row grid constants derived from the calibration statistics.  Forward

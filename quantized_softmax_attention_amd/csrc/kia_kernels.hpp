@@ -42,7 +42,7 @@ struct BwdArgs {
     float* dk;
     float* dv;
     float* probs;        // key-major P tiles
-    float* dscores;      // key-major direct dS tiles
+    float* dscores;      // key-major dS tiles (calibration terms folded in)
     float* row_cm;
     float* row_cn;
     int BH, T, n_t, K;
@@ -58,7 +58,6 @@ struct FwdConfig {
 hipError_t launch_forward(const FwdConfig& c, const FwdArgs& a, hipStream_t s);
 hipError_t launch_backward_rows(const FwdConfig& c, const BwdArgs& a, hipStream_t s);
 hipError_t launch_backward_cols(int d, const BwdArgs& a, hipStream_t s);
-hipError_t launch_backward_scatter(int d, const BwdArgs& a, hipStream_t s);
 hipError_t launch_tiles_to_dense(int BH, int T, const float* tiles, int key_major, float* dense,
                                  hipStream_t s);
 
