@@ -31,6 +31,8 @@
 //   full adds C_m at the argmax and C_n at the argmin; detach adds neither;
 //   max-only / min-only add one.  Degenerate rows: dS = P (dP - delta), no C;
 //   a row with a single causal key has P = 1 identically and dS = 0.
+#include <type_traits>
+
 #include "kia_common.hpp"
 #include "kia_kernels.hpp"
 
@@ -39,14 +41,16 @@ namespace kia {
 template <int D, int CAL, int REC, bool PROB>
 __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows_kernel(BwdArgs a) {
     constexpr int NB = D / 32;
-    using ST = StreamTile<D>;
-    constexpr int BUF = ST::kRM + ST::kTR;  // V row-major, then K transposed
+    using LT = LdsTile<D>;
+    constexpr int BUF = 2 * LT::kFloats;    // V tile, then K tile
     constexpr int XS = 36;                  // row stride of the per-wave transpose scratch
+    constexpr int NSTAGE = 2 * (D / 32);     // direct LDS loads per wave for one staged V + K pair
     __shared__ __attribute__((aligned(16))) float lds[2 * BUF];
     __shared__ __attribute__((aligned(16))) float xpose[kWaves * kTile * XS];
+    __shared__ __attribute__((aligned(16))) float sbuf[kWaves * kTileElems];  // each wave's next score tile
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
     const int li = lane & 31, hl = lane >> 5;
     const int T = a.T, n_t = a.n_t;
     const int n_blk = (n_t + kBlockTiles - 1) / kBlockTiles;
@@ -66,6 +70,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
     float* ptiles = a.probs + tile0;
     float* dstiles = a.dscores + tile0;
     float* xw = xpose + wave * kTile * XS;
+    float* sw = sbuf + wave * kTileElems;
 
     // B operand of dP^T = V dO^T (dO row of this lane's query), and delta.
     const float* oe = (REC == REC_NEAREST && PROB) ? a.o_lerp : a.o;
@@ -96,67 +101,78 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
     // a row with a single causal key has P = 1 whatever its score: zero gradient
     const float invWe = (qrow == 0) ? 0.f : ((REC == REC_NEAREST && PROB) ? 1.f / WL : invW);
 
-    float SA = 0.f, SB = 0.f;  // row sums of the direct term and of dL/dw * Wd
+    float SA = 0.f, SB = 0.f;  // row sums of the direct term and of dL/dw * Wd (Wd = g * t)
     f32x16 dq[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) dq[b] = f32x16{};
 
-    ST sv_, sk_;
-    sv_.load_rm(V, 0, T, tid);
-    sk_.load_tr(Kp, 0, T, tid);
-    sv_.store_rm(lds, tid);
-    sk_.store_tr(lds + ST::kRM, tid);
-    f32x4 snext[4];
-    if (active) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) snext[p] = *(const f32x4*)(stiles + p * 256 + lane * 4);
-    }
+    LT::load(lds, V, 0, T, tid);
+    LT::load(lds + LT::kFloats, Kp, 0, T, tid);
+    if (active) dma_tile(sw, stiles, lane);
+    wait_vmcnt<0>();
     __syncthreads();
 
+    float scur[16];
     for (int kt = 0; kt <= kt_end; ++kt) {
         const float* vcur = lds + (kt & 1) * BUF;
-        const float* kcur = vcur + ST::kRM;
+        const float* kcur = vcur + LT::kFloats;
         if (kt < kt_end) {
-            sv_.load_rm(V, (kt + 1) * kTile, T, tid);
-            sk_.load_tr(Kp, (kt + 1) * kTile, T, tid);
+            float* nxt = lds + ((kt + 1) & 1) * BUF;
+            LT::load(nxt, V, (kt + 1) * kTile, T, tid);
+            LT::load(nxt + LT::kFloats, Kp, (kt + 1) * kTile, T, tid);
         }
-        if (active && kt <= qt) {
+        const bool work = active && kt <= qt;
+        const bool prefetch = active && kt < qt;
+        if (work) {
             const int k0 = kt * kTile;
-            float sv[16];
-#pragma unroll
-            for (int p = 0; p < 4; ++p)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) sv[4 * p + j] = snext[p][j];
-            if (kt < qt) {
-                const float* tp = stiles + (size_t)(kt + 1) * kTileElems;
-#pragma unroll
-                for (int p = 0; p < 4; ++p) snext[p] = *(const f32x4*)(tp + p * 256 + lane * 4);
+            // scores of this tile: direct-loaded during the previous tile, before
+            // its 8 P / dS stores and this tile's staging loads
+            if (kt == 0) {
+                if (kt < kt_end) wait_vmcnt<NSTAGE>();
+                else wait_vmcnt<0>();
+            } else {
+                if (kt < kt_end) wait_vmcnt<NSTAGE + 8>();
+                else wait_vmcnt<8>();
             }
+            read_tile(sw, lane, scur);
+            if (prefetch) {
+                wait_lgkm0();
+                dma_tile(sw, stiles + (size_t)(kt + 1) * kTileElems, lane);
+            }
+            f32x4 xv[D / 8];
+#pragma unroll
+            for (int p = 0; p < D / 8; ++p) xv[p] = *(const f32x4*)(vcur + LT::off(li, 8 * p + 4 * hl));
             // dP^T = V dO^T : A operand row = key
             f32x16 dp = {};
 #pragma unroll
-            for (int p = 0; p < D / 8; ++p) {
-                const f32x4 x = *(const f32x4*)(vcur + rm_off<D>(li, 8 * p + 4 * hl));
+            for (int s2 = 0; s2 < D / 2; ++s2) dp = mfma32x32x2(xv[s2 >> 2][s2 & 3], dof[s2], dp);
+            // K^T operands of the dQ product (column reads), read while the elementwise work runs
+            float xk[16 * NB];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) dp = mfma32x32x2(x[j], dof[4 * p + j], dp);
-            }
+            for (int s2 = 0; s2 < 16 * NB; ++s2) xk[s2] = kcur[LT::off(acc_row(s2 & 15, hl), 32 * (s2 >> 4) + li)];
 
             float ds[16], pr[16];
+            auto grads = [&](auto diag_t) {
+                constexpr bool DIAG = decltype(diag_t)::value;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = k0 + acc_row(r, hl);
-                const bool valid = qvalid && key <= qrow;
-                const Recon e = reconstruct<CAL, REC == REC_NEAREST>(rg, sv[r]);
-                const bool keep = valid && e.inwin;
-                const float wh = (REC == REC_LERP) ? e.wl : e.wn;
-                pr[r] = keep ? wh * invW : 0.f;
-                const float gt = (dp[r] - dlt) * invWe;
-                const float A = gt * e.g * rg.coh;
-                const float Wd = e.g * fmaf(rg.coh - 1.f, e.uc, e.f * (e.fi + 1.f) * rg.c);
-                ds[r] = keep ? A : 0.f;
-                SA += ds[r];
-                SB += keep ? gt * Wd : 0.f;
-            }
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + acc_row(r, hl);
+                    const bool valid = DIAG ? key <= qrow : true;
+                    const Recon e = reconstruct<CAL, REC == REC_NEAREST>(rg, scur[r]);
+                    const bool keep = valid && e.inwin;
+                    const float wh = (REC == REC_LERP) ? e.wl : e.wn;
+                    pr[r] = (keep && qvalid) ? wh * invW : 0.f;
+                    // dL/dw times the grid value; the direct term and the h-derivative share it
+                    const float gtg = (dp[r] - dlt) * invWe * e.g;
+                    const float A = gtg * rg.coh;
+                    const float t = fmaf(rg.cohm1, e.u, e.f * fmaf(e.fi, rg.c, rg.c));
+                    ds[r] = keep ? A : 0.f;
+                    SA += ds[r];
+                    SB = keep ? fmaf(gtg, t, SB) : SB;
+                }
+            };
+            if (kt == qt) grads(std::true_type{});
+            else grads(std::false_type{});
 
             // P and dS to key-major tiles through the wave's LDS scratch
             float* pp = ptiles + (size_t)kt * kTileElems;
@@ -178,19 +194,18 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
 
             // dQ^T += K^T dS^T : A operand row = head-dim index
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const f32x4 x = *(const f32x4*)(kcur + tr_off(32 * b + li, 8 * p + 4 * hl));
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) dq[b] = mfma32x32x2(x[j], ds[4 * p + j], dq[b]);
-                }
+            for (int s2 = 0; s2 < 16 * NB; ++s2) {
+                const int b = s2 >> 4, kk = s2 & 15;
+                dq[b] = mfma32x32x2(xk[s2], ds[kk], dq[b]);
             }
         }
-        if (kt < kt_end) {
-            float* nxt = lds + ((kt + 1) & 1) * BUF;
-            sv_.store_rm(nxt, tid);
-            sk_.store_tr(nxt + ST::kRM, tid);
+        // the staging loads were issued first; the score prefetch (4) and the
+        // P / dS stores (8) may stay in flight
+        if (work) {
+            if (prefetch) wait_vmcnt<12>();
+            else wait_vmcnt<8>();
+        } else {
+            wait_vmcnt<0>();
         }
         __syncthreads();
     }
@@ -249,12 +264,14 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
 template <int D>
 __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_cols_kernel(BwdArgs a) {
     constexpr int NB = D / 32;
-    using ST = StreamTile<D>;
-    constexpr int BUF = 2 * ST::kTR;  // dO^T, then Q^T
+    using LT = LdsTile<D>;
+    constexpr int BUF = 2 * LT::kFloats;  // dO tile, then Q tile
+    constexpr int NSTAGE = 2 * (D / 32);  // direct LDS loads per wave for one staged dO + Q pair
     __shared__ __attribute__((aligned(16))) float lds[2 * BUF];
+    __shared__ __attribute__((aligned(16))) float pdbuf[kWaves * 2 * kTileElems];  // each wave's next P, dS tiles
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
     const int li = lane & 31, hl = lane >> 5;
     const int T = a.T, n_t = a.n_t;
     const int n_blk = (n_t + kBlockTiles - 1) / kBlockTiles;
@@ -274,62 +291,60 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_cols
 #pragma unroll
     for (int b = 0; b < NB; ++b) { dv[b] = f32x16{}; dk[b] = f32x16{}; }
 
-    ST so_, sq_;
-    so_.load_tr(dO, qt_begin * kTile, T, tid);
-    sq_.load_tr(Q, qt_begin * kTile, T, tid);
-    so_.store_tr(lds, tid);
-    sq_.store_tr(lds + ST::kTR, tid);
-    f32x4 pnext[4], dnext[4];
-    if (active) {
-        const size_t toff = (hbase + tile_index(kt, kt)) * kTileElems;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            pnext[p] = *(const f32x4*)(a.probs + toff + p * 256 + lane * 4);
-            dnext[p] = *(const f32x4*)(a.dscores + toff + p * 256 + lane * 4);
-        }
-    }
+    float* pw = pdbuf + wave * 2 * kTileElems;
+    float* dw = pw + kTileElems;
+    LT::load(lds, dO, qt_begin * kTile, T, tid);
+    LT::load(lds + LT::kFloats, Q, qt_begin * kTile, T, tid);
+    auto dma_pd = [&](int qt_t) {
+        const size_t toff = (hbase + tile_index(qt_t, kt)) * kTileElems;
+        dma_tile(pw, a.probs + toff, lane);
+        dma_tile(dw, a.dscores + toff, lane);
+    };
+    if (active) dma_pd(kt);
+    wait_vmcnt<0>();
     __syncthreads();
 
+    float pc[16], dc[16];
     for (int qt = qt_begin; qt < n_t; ++qt) {
         const float* ocur = lds + (qt & 1) * BUF;
-        const float* qcur = ocur + ST::kTR;
+        const float* qcur = ocur + LT::kFloats;
         if (qt + 1 < n_t) {
-            so_.load_tr(dO, (qt + 1) * kTile, T, tid);
-            sq_.load_tr(Q, (qt + 1) * kTile, T, tid);
+            float* nxt = lds + ((qt + 1) & 1) * BUF;
+            LT::load(nxt, dO, (qt + 1) * kTile, T, tid);
+            LT::load(nxt + LT::kFloats, Q, (qt + 1) * kTile, T, tid);
         }
-        if (active && qt >= kt) {
-            float pv[16], dsv[16];
-#pragma unroll
-            for (int p = 0; p < 4; ++p)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) { pv[4 * p + j] = pnext[p][j]; dsv[4 * p + j] = dnext[p][j]; }
-            if (qt + 1 < n_t) {
-                const size_t toff = (hbase + tile_index(qt + 1, kt)) * kTileElems;
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    pnext[p] = *(const f32x4*)(a.probs + toff + p * 256 + lane * 4);
-                    dnext[p] = *(const f32x4*)(a.dscores + toff + p * 256 + lane * 4);
-                }
+        const bool work = active && qt >= kt;
+        const bool prefetch = work && qt + 1 < n_t;
+        if (work) {
+            // this tile's P and dS: direct-loaded during the previous tile, before
+            // this tile's staging loads
+            if (qt + 1 < n_t) wait_vmcnt<NSTAGE>();
+            else wait_vmcnt<0>();
+            read_tile(pw, lane, pc);
+            read_tile(dw, lane, dc);
+            if (prefetch) {
+                wait_lgkm0();
+                dma_pd(qt + 1);
             }
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
+                // dO^T and Q^T operands: lane = head-dim column, one float per query
+                float xo[16], xq[16];
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const f32x4 x = *(const f32x4*)(ocur + tr_off(32 * b + li, 8 * p + 4 * hl));
-                    const f32x4 y = *(const f32x4*)(qcur + tr_off(32 * b + li, 8 * p + 4 * hl));
+                for (int kk = 0; kk < 16; ++kk) {
+                    xo[kk] = ocur[LT::off(acc_row(kk, hl), 32 * b + li)];
+                    xq[kk] = qcur[LT::off(acc_row(kk, hl), 32 * b + li)];
+                }
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        dv[b] = mfma32x32x2(x[j], pv[4 * p + j], dv[b]);
-                        dk[b] = mfma32x32x2(y[j], dsv[4 * p + j], dk[b]);
-                    }
+                for (int kk = 0; kk < 16; ++kk) {
+                    dv[b] = mfma32x32x2(xo[kk], pc[kk], dv[b]);
+                    dk[b] = mfma32x32x2(xq[kk], dc[kk], dk[b]);
                 }
             }
         }
-        if (qt + 1 < n_t) {
-            float* nxt = lds + ((qt + 1) & 1) * BUF;
-            so_.store_tr(nxt, tid);
-            sq_.store_tr(nxt + ST::kTR, tid);
-        }
+        // the staging loads were issued first; the P / dS prefetch (8) may stay in flight
+        if (prefetch) wait_vmcnt<8>();
+        else wait_vmcnt<0>();
         __syncthreads();
     }
     if (active && krow < T) {

@@ -69,12 +69,16 @@ constexpr int kBlockTiles = kWaves;  // stationary 32-row tiles per workgroup
 
 // LDS layouts of a streamed 32 x D tile (rows r of a row-major [T][D] tensor):
 //  row-major  rm(r, c) = r*(D+4) + c: lane = row, float4 along c (no conflicts)
-//  transposed tr(c, r) = c*32 + 4*((r/4) ^ (c%8)) + r%4: lane = column c,
-//             float4 along 4 consecutive rows; the xor spreads both the
-//             staging writes and the float4 reads over all banks.
+//  transposed tr(c, r) = c*32 + 4*((r/4) ^ ((c/2)%8)) + r%4: lane = column
+//             c, float4 along 4 consecutive rows.  With 64 banks a column of
+//             32 floats covers one bank half (c even / odd); the xor on c/2
+//             gives the 8 columns of each half that one float4 read phase
+//             touches 8 distinct 4-bank groups.
 template <int D>
 __device__ __forceinline__ int rm_off(int r, int c) { return r * (D + 4) + c; }
-__device__ __forceinline__ int tr_off(int c, int r) { return c * kTile + 4 * ((r >> 2) ^ (c & 7)) + (r & 3); }
+__device__ __forceinline__ int tr_off(int c, int r) {
+    return c * kTile + 4 * ((r >> 2) ^ ((c >> 1) & 7)) + (r & 3);
+}
 
 template <int D>
 struct StreamTile {
@@ -83,12 +87,22 @@ struct StreamTile {
     static constexpr int kTR = D * kTile;                // floats of a transposed staged tile
     f32x4 v[kF4];
 
-    // row-major staging: consecutive threads read consecutive float4 of a row
+    // row-major staging: consecutive threads read consecutive float4 of a row.
+    // Rows at or past T read as zero; full tiles (the uniform common case) skip the test.
     __device__ __forceinline__ void load_rm(const float* src, int r0, int T, int tid) {
+        if (r0 + kTile <= T) {
 #pragma unroll
-        for (int i = 0; i < kF4; ++i) {
-            const int e = tid + kThreads * i, r = e / (D / 4), c4 = e % (D / 4);
-            v[i] = (r0 + r < T) ? *(const f32x4*)(src + (size_t)(r0 + r) * D + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < kF4; ++i) {
+                const int e = tid + kThreads * i, r = e / (D / 4), c4 = e % (D / 4);
+                v[i] = *(const f32x4*)(src + (size_t)(r0 + r) * D + 4 * c4);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kF4; ++i) {
+                const int e = tid + kThreads * i, r = e / (D / 4), c4 = e % (D / 4);
+                v[i] = (r0 + r < T) ? *(const f32x4*)(src + (size_t)(r0 + r) * D + 4 * c4)
+                                    : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
     }
     __device__ __forceinline__ void store_rm(float* lds, int tid) const {
@@ -100,10 +114,19 @@ struct StreamTile {
     }
     // transposed staging: a wave's lanes take 32 consecutive rows of one float4 column
     __device__ __forceinline__ void load_tr(const float* src, int r0, int T, int tid) {
+        if (r0 + kTile <= T) {
 #pragma unroll
-        for (int i = 0; i < kF4; ++i) {
-            const int e = tid + kThreads * i, r = e & 31, c4 = e >> 5;
-            v[i] = (r0 + r < T) ? *(const f32x4*)(src + (size_t)(r0 + r) * D + 4 * c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < kF4; ++i) {
+                const int e = tid + kThreads * i, r = e & 31, c4 = e >> 5;
+                v[i] = *(const f32x4*)(src + (size_t)(r0 + r) * D + 4 * c4);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kF4; ++i) {
+                const int e = tid + kThreads * i, r = e & 31, c4 = e >> 5;
+                v[i] = (r0 + r < T) ? *(const f32x4*)(src + (size_t)(r0 + r) * D + 4 * c4)
+                                    : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
     }
     __device__ __forceinline__ void store_tr(float* lds, int tid) const {
@@ -115,6 +138,75 @@ struct StreamTile {
         }
     }
 };
+
+// A 32 x D tile of a row-major [T][D] tensor staged in LDS by the whole
+// workgroup with direct global -> LDS loads (global_load_lds_dwordx4: each
+// lane's 16 bytes land at slot lane of a 1 KB chunk, no registers involved).
+// We choose which float4 of the tile each lane fetches, so the slots can be
+// swizzled: float4 column c4 of row r sits at slot r*(D/4) + (c4 ^ swz(r)),
+// swz a permutation of r's low 4 bits with bit 3 = bit 2 of r.  Then
+//  - a row read (lane = row, one float4) by 16 lanes hits 16 distinct 4-bank
+//    groups, and
+//  - a column read (lane = column, one float) by 64 lanes whose two halves
+//    take rows r and r+4 (r%8 < 4) hits 64 distinct banks.
+// Rows at or past T are fetched from row T-1 (finite, and every consumer
+// multiplies them by a zero weight, probability or score gradient).
+template <int D>
+struct LdsTile {
+    static constexpr int kF4Row = D / 4;
+    static constexpr int kFloats = kTile * D;
+    static __device__ __forceinline__ int swz(int r) {
+        return (r & 3) | (((r >> 3) & 1) << 2) | (((r >> 2) & 1) << 3);
+    }
+    static __device__ __forceinline__ int off(int r, int c) {
+        return (r * kF4Row + ((c >> 2) ^ swz(r))) * 4 + (c & 3);
+    }
+    static __device__ __forceinline__ void load(float* lds_tile, const float* src, int r0, int T, int tid) {
+        const int wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+        for (int k = 0; k < D / 32; ++k) {
+            const int i = wave + kWaves * k;  // 1 KB chunk index
+            const int slot = i * kWave + lane;
+            const int r = slot / kF4Row;
+            const int c4 = (slot % kF4Row) ^ swz(r);
+            const float* g = src + (size_t)min(r0 + r, T - 1) * D + 4 * c4;
+            __builtin_amdgcn_global_load_lds((const void*)g, (__attribute__((address_space(3))) void*)(lds_tile + i * 256),
+                                             16, 0, 0);
+        }
+    }
+};
+
+// Direct global -> LDS copy of one wave's 4 KB fragment-native tile (the
+// score, probability and score-gradient tiles): lane l fetches its float4 of
+// each 1 KB chunk, which lands at the same place in the wave's LDS slot, so
+// the lane later reads back exactly the registers it would have loaded.
+__device__ __forceinline__ void dma_tile(float* lds_wave, const float* src, int lane) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        __builtin_amdgcn_global_load_lds((const void*)(src + p * 256 + lane * 4),
+                                         (__attribute__((address_space(3))) void*)(lds_wave + p * 256), 16, 0, 0);
+}
+__device__ __forceinline__ void read_tile(const float* lds_wave, int lane, float* out) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const f32x4 x = *(const f32x4*)(lds_wave + p * 256 + lane * 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) out[4 * p + j] = x[j];
+    }
+}
+
+// Wait until at most N vector memory operations of this wave are outstanding
+// (lgkm and exp counters left free).  Vector memory operations complete in
+// issue order, so this waits for everything issued before the last N.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Wait until this wave's LDS operations have completed (vector memory and
+// export counters left free).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0x0F | (0x7 << 4) | (0x3 << 14)); }
 
 // Heaviest-first work order over (slice, 128-row block) pairs.  Blocks of one
 // slice share K and V; workgroups are dealt round-robin to the 8 XCDs, so when
@@ -135,6 +227,32 @@ __device__ __forceinline__ void map_block(int g, int BH, int nb, bool descending
     if (descending) blk = nb - 1 - blk;
 }
 
+// Interleave NS matrix steps with NE vector steps (NE <= NS), spreading the
+// vector steps evenly, so one wavefront keeps its matrix pipe busy while its
+// vector ALU works on independent data (another tile's elementwise math).
+template <int NS, int NE, typename FM, typename FV>
+__device__ __forceinline__ void interleave(FM&& fm, FV&& fv) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        fm(s);
+#pragma unroll
+        for (int e = s * NE / NS; e < (s + 1) * NE / NS; ++e) fv(e);
+    }
+}
+
+// Ask the scheduler to keep the interleave: NS groups of one matrix
+// instruction followed by up to VPER vector ALU instructions.  Must sit in the
+// same basic block as the code it orders.
+template <int NS, int VPER, int NREAD = 0>
+__device__ __forceinline__ void pin_interleave() {
+    if (NREAD > 0) __builtin_amdgcn_sched_group_barrier(0x100, NREAD, 0);  // LDS reads first
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);  // VALU
+    }
+}
+
 // Per-row grid constants derived from the calibration statistics.  Forward
 // and backward both call this, so they see bitwise identical constants.
 struct RowGrid {
@@ -143,6 +261,7 @@ struct RowGrid {
     float hl2;    // h * log2(e), so exp(-j h) = exp2(-j * hl2)
     float c;      // 1 - exp(-h): relative drop across one interval
     float coh;    // c / h (1 in the degenerate branch: the h -> 0 limit)
+    float cohm1;  // c / h - 1
     float Kf;     // K as float
     bool degen;
 };
@@ -171,32 +290,38 @@ __device__ __forceinline__ RowGrid make_row_grid(float m, float n, int K, float 
         g.c = -expm1f(-h);
         g.coh = g.c * g.invh;
     }
+    g.cohm1 = g.coh - 1.f;
     return g;
 }
 
-// Reconstruction of one score.  uc = min(u, K) with u = (m - s)/h; LERP
-// segment i = min(floor(uc), K-1), f = uc - i, weight g_i (1 - f c) where
-// g_i = exp(-i h) is grid value i; Nearest grid point r = floor(uc + 1/2),
-// weight g_r.  `inwin` is the FWM window test u <= K (always true for
-// MinMax).
+// exp2 on the hardware transcendental unit.  Results below the fp32 normal
+// range (weights under 1.2e-38, i.e. more than 87 nats below the row max)
+// may flush to zero; that changes a normalised probability by less than
+// 1e-38 relative.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Reconstruction of one score.  u = (m - s)/h >= 0 (distance below the row
+// max in grid steps); LERP segment i = min(floor(u), K-1), f = u - i, weight
+// g_i (1 - f c) where g_i = exp(-i h) is grid value i; Nearest grid point
+// r = floor(u + 1/2), weight g_r.  Under MinMax u <= K up to one rounding
+// (the row min), which segment K-1 absorbs; under FWM keys with u > K are
+// outside the window (`inwin`) and get weight 0.
 struct Recon {
-    float uc, fi, f, g, wl, wn;
+    float u, fi, f, g, wl, wn;
     bool inwin;
 };
 
 template <int CAL, bool NEED_NEAREST>
 __device__ __forceinline__ Recon reconstruct(const RowGrid& rg, float s) {
     Recon e;
-    float u = (rg.m - s) * rg.invh;
-    e.inwin = (CAL == CAL_MINMAX) ? true : (u <= rg.Kf);
-    e.uc = fminf(u, rg.Kf);
-    e.fi = fminf(fmaxf(floorf(e.uc), 0.f), rg.Kf - 1.f);
-    e.f = e.uc - e.fi;
-    e.g = exp2f(-e.fi * rg.hl2);
+    e.u = (rg.m - s) * rg.invh;
+    e.inwin = (CAL == CAL_MINMAX) ? true : (e.u <= rg.Kf);
+    e.fi = fminf(floorf(e.u), rg.Kf - 1.f);
+    e.f = e.u - e.fi;
+    e.g = fast_exp2(-e.fi * rg.hl2);
     e.wl = e.g * fmaf(-e.f, rg.c, 1.f);
     if (NEED_NEAREST) {
-        float fr = floorf(e.uc + 0.5f);
-        e.wn = exp2f(-fr * rg.hl2);
+        e.wn = fast_exp2(-floorf(e.u + 0.5f) * rg.hl2);
     } else {
         e.wn = 0.f;
     }

@@ -15,21 +15,25 @@
 //            sum W, accumulate O^T += V^T W^T on the matrix cores.
 // Operator: "Pretraining Transformers with Quantized Softmax in Attention"
 // (paperlayer digest), section 3 "Calibration" / "Reconstruction" and App. A.
+#include <type_traits>
+
 #include "kia_common.hpp"
 #include "kia_kernels.hpp"
 
 namespace kia {
 
 template <int D, int CAL, int REC, bool PROB, bool DUMP>
-__global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_forward_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forward_kernel(FwdArgs a) {
     static_assert(D % 32 == 0, "head dim must be a multiple of 32");
     constexpr int NB = D / 32;  // 32-wide blocks of the head dim
-    using ST = StreamTile<D>;
-    constexpr int BUF = ST::kRM > ST::kTR ? ST::kRM : ST::kTR;
-    __shared__ __attribute__((aligned(16))) float lds[2 * BUF];
+    constexpr int NSTAGE = D / 32;  // direct LDS loads per wave for one staged tile
+    using LT = LdsTile<D>;
+    constexpr int BUF = LT::kFloats;
+    __shared__ __attribute__((aligned(16))) float lds[2 * BUF];            // K (sweep 1) / V (sweep 2) tiles
+    __shared__ __attribute__((aligned(16))) float sbuf[kWaves * kTileElems];  // each wave's next score tile
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
     const int li = lane & 31, hl = lane >> 5;
     const int T = a.T, n_t = a.n_t;
     const int n_blk = (n_t + kBlockTiles - 1) / kBlockTiles;
@@ -46,53 +50,83 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_forward_kerne
     const float* V = a.v + head;
     const int64_t tiles_per_head = (int64_t)n_t * (n_t + 1) / 2;
     float* tiles = a.tiles + ((size_t)bh * tiles_per_head + (active ? tile_index(qt, 0) : 0)) * kTileElems;
+    float* sw = sbuf + wave * kTileElems;
 
-    // B operand of S^T = K Q^T: lane holds Q[qrow][c] for c = 8p + 4*hl + j.
+    // B operand of S^T = K Q^T: lane holds Q[qrow][c] / sqrt(d) for c = 8p + 4*hl + j.
     float qf[D / 2];
 #pragma unroll
     for (int p = 0; p < D / 8; ++p) {
         f32x4 x = {0.f, 0.f, 0.f, 0.f};
         if (qvalid) x = *(const f32x4*)(Q + (size_t)qrow * D + 8 * p + 4 * hl);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) qf[4 * p + j] = x[j];
+        for (int j = 0; j < 4; ++j) qf[4 * p + j] = x[j] * a.scale;
     }
 
     // ---- sweep 1: scores, row extremes --------------------------------------
+    // K tiles arrive by direct global -> LDS loads one tile ahead.  Per wave
+    // the matrix instructions of key tile kt interleave with the extreme
+    // tracking and the score store of tile kt-1.  Each lane walks its keys in
+    // increasing order, so a strict comparison keeps the lowest index among
+    // equal extremes.  Only a wave's last tile (the diagonal) needs the causal
+    // mask; lanes past the end of the sequence compute values never stored as
+    // results.
     float m = -INFINITY, n = INFINITY;
     int am = 0, an = 0;
-    ST st;
-    st.load_rm(Kp, 0, T, tid);
-    st.store_rm(lds, tid);
+    auto track = [&](const f32x16& acc, int kt_t, auto diag_t, int r) {
+        constexpr bool DIAG = decltype(diag_t)::value;
+        const int key = kt_t * kTile + acc_row(r, hl);
+        const float sc = acc[r];
+        const bool valid = DIAG ? key <= qrow : true;
+        const bool gt = valid && sc > m;
+        m = gt ? sc : m;
+        am = gt ? key : am;
+        if (CAL == CAL_MINMAX) {
+            const bool lt = valid && sc < n;
+            n = lt ? sc : n;
+            an = lt ? key : an;
+        }
+        if ((r & 3) == 3) {
+            const int p = r >> 2;
+            f32x4 x;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool ok = DIAG ? (kt_t * kTile + acc_row(4 * p + j, hl)) <= qrow : true;
+                x[j] = ok ? acc[4 * p + j] : 0.f;
+            }
+            *(f32x4*)(tiles + (size_t)kt_t * kTileElems + p * 256 + lane * 4) = x;
+        }
+    };
+    LT::load(lds, Kp, 0, T, tid);
+    wait_vmcnt<0>();
     __syncthreads();
+    f32x16 accp = {};
     for (int kt = 0; kt <= kt_end; ++kt) {
         const float* cur = lds + (kt & 1) * BUF;
-        if (kt < kt_end) st.load_rm(Kp, (kt + 1) * kTile, T, tid);
+        if (kt < kt_end) LT::load(lds + ((kt + 1) & 1) * BUF, Kp, (kt + 1) * kTile, T, tid);
+        const bool stores = active && kt <= qt && kt > 0;
         if (active && kt <= qt) {
-            const int k0 = kt * kTile;
+            f32x4 xk[D / 8];
+#pragma unroll
+            for (int p = 0; p < D / 8; ++p) xk[p] = *(const f32x4*)(cur + LT::off(li, 8 * p + 4 * hl));
             f32x16 acc = {};
+            auto mstep = [&](int s) { acc = mfma32x32x2(xk[s >> 2][s & 3], qf[s], acc); };
+            if (kt > 0) {
+                interleave<D / 2, 16>(mstep, [&](int r) { track(accp, kt - 1, std::false_type{}, r); });
+                pin_interleave<D / 2, 4, D / 8>();
+            } else {
 #pragma unroll
-            for (int p = 0; p < D / 8; ++p) {
-                const f32x4 x = *(const f32x4*)(cur + rm_off<D>(li, 8 * p + 4 * hl));
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc = mfma32x32x2(x[j], qf[4 * p + j], acc);
+                for (int s = 0; s < D / 2; ++s) mstep(s);
             }
-            float sv[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = k0 + acc_row(r, hl);
-                const float s = acc[r] * a.scale;
-                const bool valid = qvalid && key <= qrow;
-                if (valid && s > m) { m = s; am = key; }
-                if (CAL == CAL_MINMAX && valid && s < n) { n = s; an = key; }
-                sv[r] = valid ? s : 0.f;
-            }
-            float* tp = tiles + (size_t)kt * kTileElems;
-#pragma unroll
-            for (int p = 0; p < 4; ++p)
-                *(f32x4*)(tp + p * 256 + lane * 4) = f32x4{sv[4 * p], sv[4 * p + 1], sv[4 * p + 2], sv[4 * p + 3]};
+            accp = acc;
         }
-        if (kt < kt_end) st.store_rm(lds + ((kt + 1) & 1) * BUF, tid);
+        // the K tile loads were issued first; the 4 score stores may stay in flight
+        if (stores) wait_vmcnt<4>();
+        else wait_vmcnt<0>();
         __syncthreads();
+    }
+    if (active) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) track(accp, qt, std::true_type{}, r);
     }
     // the two lane halves of a query saw disjoint keys: merge, lowest index on ties
     {
@@ -109,6 +143,10 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_forward_kerne
     const RowGrid rg = make_row_grid(m, n, a.K, a.tau, CAL);
 
     // ---- sweep 2: reconstruct, normalise, O = W V / sum(W) -----------------
+    // V tiles arrive like the K tiles; each wave's next score tile arrives by a
+    // direct load into its LDS slot.  Per wave the matrix instructions of
+    // tile kt (weights already computed) interleave with the reconstruction of
+    // tile kt+1.
     float W = 0.f, WL = 0.f;
     f32x16 oacc[NB];
     f32x16 olacc[PROB ? NB : 1];
@@ -117,61 +155,87 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_forward_kerne
 #pragma unroll
     for (int b = 0; b < (PROB ? NB : 1); ++b) olacc[b] = f32x16{};
 
-    st.load_tr(V, 0, T, tid);
-    st.store_tr(lds, tid);
-    f32x4 snext[4];
+    float sv[16], w[16], wl[16], wn[16], wln[16];
+    auto recon = [&](int kt_t, auto diag_t, int r) {
+        constexpr bool DIAG = decltype(diag_t)::value;
+        const int key = kt_t * kTile + acc_row(r, hl);
+        const bool valid = DIAG ? key <= qrow : true;
+        const Recon e = reconstruct<CAL, REC == REC_NEAREST>(rg, sv[r]);
+        const bool keep = valid && e.inwin;
+        const float wh = (REC == REC_LERP) ? e.wl : e.wn;
+        wn[r] = keep ? wh : 0.f;
+        W += wn[r];
+        wln[r] = keep ? e.wl : 0.f;
+        if (REC == REC_NEAREST) WL += wln[r];
+        if (DUMP && qvalid && valid) {
+            int idx = (REC == REC_LERP) ? (int)e.fi : (int)floorf(e.u + 0.5f);
+            if (!e.inwin) idx = -1;
+            a.idx_dump[((size_t)bh * T + qrow) * T + key] = idx;
+        }
+    };
+
+    LT::load(lds, V, 0, T, tid);
     if (active) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) snext[p] = *(const f32x4*)(tiles + p * 256 + lane * 4);
+        for (int p = 0; p < 4; ++p) {
+            const f32x4 x = *(const f32x4*)(tiles + p * 256 + lane * 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sv[4 * p + j] = x[j];
+        }
+        if (qt > 0) dma_tile(sw, tiles + kTileElems, lane);
+        if (qt == 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) recon(0, std::true_type{}, r);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) recon(0, std::false_type{}, r);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { w[r] = wn[r]; wl[r] = wln[r]; }
     }
+    wait_vmcnt<0>();
     __syncthreads();
     for (int kt = 0; kt <= kt_end; ++kt) {
         const float* cur = lds + (kt & 1) * BUF;
-        if (kt < kt_end) st.load_tr(V, (kt + 1) * kTile, T, tid);
+        if (kt < kt_end) LT::load(lds + ((kt + 1) & 1) * BUF, V, (kt + 1) * kTile, T, tid);
+        const bool more = active && kt + 1 <= qt;      // tile kt+1 exists for this wave
+        const bool prefetch = active && kt + 2 <= qt;  // and tile kt+2
         if (active && kt <= qt) {
-            const int k0 = kt * kTile;
-            float sv[16];
-#pragma unroll
-            for (int p = 0; p < 4; ++p)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) sv[4 * p + j] = snext[p][j];
-            if (kt < qt) {
-                const float* tp = tiles + (size_t)(kt + 1) * kTileElems;
-#pragma unroll
-                for (int p = 0; p < 4; ++p) snext[p] = *(const f32x4*)(tp + p * 256 + lane * 4);
-            }
-            float w[16], wl[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = k0 + acc_row(r, hl);
-                const bool valid = qvalid && key <= qrow;
-                const Recon e = reconstruct<CAL, REC == REC_NEAREST>(rg, sv[r]);
-                const bool keep = valid && e.inwin;
-                const float wh = (REC == REC_LERP) ? e.wl : e.wn;
-                w[r] = keep ? wh : 0.f;
-                W += w[r];
-                wl[r] = keep ? e.wl : 0.f;
-                if (REC == REC_NEAREST) WL += wl[r];
-                if (DUMP && valid) {
-                    int idx = (REC == REC_LERP) ? (int)e.fi : (int)floorf(e.uc + 0.5f);
-                    if (!e.inwin) idx = -1;
-                    a.idx_dump[((size_t)bh * T + qrow) * T + key] = idx;
+            if (more) {
+                // scores of tile kt+1 (direct-loaded during the previous tile)
+                if (kt < kt_end) wait_vmcnt<NSTAGE>();
+                else wait_vmcnt<0>();
+                read_tile(sw, lane, sv);
+                if (prefetch) {
+                    wait_lgkm0();
+                    dma_tile(sw, tiles + (size_t)(kt + 2) * kTileElems, lane);
                 }
             }
+            // V^T operand: lane = head-dim column, one float per key (column reads)
+            float xv[16 * NB];
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
+            for (int s2 = 0; s2 < 16 * NB; ++s2) xv[s2] = cur[LT::off(acc_row(s2 & 15, hl), 32 * (s2 >> 4) + li)];
+            auto mstep = [&](int s) {
+                const int b = s >> 4, kk = s & 15;
+                oacc[b] = mfma32x32x2(xv[s], w[kk], oacc[b]);
+                if (PROB) olacc[b] = mfma32x32x2(xv[s], wl[kk], olacc[b]);
+            };
+            if (kt + 1 < qt) {
+                interleave<16 * NB, 16>(mstep, [&](int r) { recon(kt + 1, std::false_type{}, r); });
+                pin_interleave<16 * NB, (PROB ? 4 : 6) * 2 / NB, 16 * NB>();
+            } else if (kt + 1 == qt) {
+                interleave<16 * NB, 16>(mstep, [&](int r) { recon(kt + 1, std::true_type{}, r); });
+                pin_interleave<16 * NB, (PROB ? 4 : 6) * 2 / NB, 16 * NB>();
+            } else {
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const f32x4 x = *(const f32x4*)(cur + tr_off(32 * b + li, 8 * p + 4 * hl));
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        oacc[b] = mfma32x32x2(x[j], w[4 * p + j], oacc[b]);
-                        if (PROB) olacc[b] = mfma32x32x2(x[j], wl[4 * p + j], olacc[b]);
-                    }
-                }
+                for (int s = 0; s < 16 * NB; ++s) mstep(s);
             }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) { w[r] = wn[r]; wl[r] = wln[r]; }
         }
-        if (kt < kt_end) st.store_tr(lds + ((kt + 1) & 1) * BUF, tid);
+        // the V tile loads were issued first; the score prefetch may stay in flight
+        if (prefetch) wait_vmcnt<4>();
+        else wait_vmcnt<0>();
         __syncthreads();
     }
     W += __shfl_xor(W, 32);

@@ -81,10 +81,11 @@ def gpu_slice(gpu, b, h):
 
 def score_bound(Qh, Kh):
     """A-priori bound on |fp32 score - exact score| per pair: a length-d fp32
-    dot product plus the scale multiply, (d + 2) * 2^-24 * sum_c |Q_c K_c| / sqrt(d)."""
+    dot product, the scale applied to Q and the final rounding,
+    (d + 3) * 2^-24 * sum_c |Q_c K_c| / sqrt(d)."""
     d = Qh.shape[1]
     absdot = np.abs(Qh.astype(np.float64)) @ np.abs(Kh.astype(np.float64)).T / np.sqrt(d)
-    return (d + 2) * 2.0 ** -24 * absdot
+    return (d + 3) * 2.0 ** -24 * absdot
 
 
 class SliceCheck:
