@@ -207,7 +207,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
         } else {
             wait_vmcnt<0>();
         }
-        __syncthreads();
+        lds_barrier();
     }
 
     SA += __shfl_xor(SA, 32);
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_cols
         // the staging loads were issued first; the P / dS prefetch (8) may stay in flight
         if (prefetch) wait_vmcnt<8>();
         else wait_vmcnt<0>();
-        __syncthreads();
+        lds_barrier();
     }
     if (active && krow < T) {
         float* dkrow = a.dk + head + (size_t)krow * D;

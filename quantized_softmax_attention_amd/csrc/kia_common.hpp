@@ -151,6 +151,17 @@ struct StreamTile {
 //    take rows r and r+4 (r%8 < 4) hits 64 distinct banks.
 // Rows at or past T are fetched from row T-1 (finite, and every consumer
 // multiplies them by a zero weight, probability or score gradient).
+// LDS destination of a direct global -> LDS load.  The address passes through
+// an empty asm statement, so the compiler keeps no alias scope for the load's
+// LDS target: it then orders the load conservatively against every LDS access
+// but does not insert its own vmcnt waits before reads of other buffers.  The
+// kernels order these loads with explicit wait_vmcnt + barrier pairs.
+__device__ __forceinline__ __attribute__((address_space(3))) void* lds_dst(float* p) {
+    uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)p;
+    asm volatile("" : "+v"(a));
+    return (__attribute__((address_space(3))) void*)(uintptr_t)a;
+}
+
 template <int D>
 struct LdsTile {
     static constexpr int kF4Row = D / 4;
@@ -170,7 +181,7 @@ struct LdsTile {
             const int r = slot / kF4Row;
             const int c4 = (slot % kF4Row) ^ swz(r);
             const float* g = src + (size_t)min(r0 + r, T - 1) * D + 4 * c4;
-            __builtin_amdgcn_global_load_lds((const void*)g, (__attribute__((address_space(3))) void*)(lds_tile + i * 256),
+            __builtin_amdgcn_global_load_lds((const void*)g, lds_dst(lds_tile + i * 256),
                                              16, 0, 0);
         }
     }
@@ -183,8 +194,8 @@ struct LdsTile {
 __device__ __forceinline__ void dma_tile(float* lds_wave, const float* src, int lane) {
 #pragma unroll
     for (int p = 0; p < 4; ++p)
-        __builtin_amdgcn_global_load_lds((const void*)(src + p * 256 + lane * 4),
-                                         (__attribute__((address_space(3))) void*)(lds_wave + p * 256), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(src + p * 256 + lane * 4), lds_dst(lds_wave + p * 256), 16,
+                                         0, 0);
 }
 __device__ __forceinline__ void read_tile(const float* lds_wave, int lane, float* out) {
 #pragma unroll
@@ -193,6 +204,16 @@ __device__ __forceinline__ void read_tile(const float* lds_wave, int lane, float
 #pragma unroll
         for (int j = 0; j < 4; ++j) out[4 * p + j] = x[j];
     }
+}
+
+// Workgroup barrier that orders LDS only.  Each wave waits for its own LDS
+// reads and writes (lgkmcnt) and then meets the others; global loads and
+// stores stay in flight.  (__syncthreads also drains vmcnt, which would retire
+// every prefetch and score store before the next tile could start.)  Direct
+// global -> LDS loads are counted by vmcnt: a wave waits for its share with
+// wait_vmcnt before calling this.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Wait until at most N vector memory operations of this wave are outstanding

@@ -29,7 +29,12 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
     constexpr int NSTAGE = D / 32;  // direct LDS loads per wave for one staged tile
     using LT = LdsTile<D>;
     constexpr int BUF = LT::kFloats;
-    __shared__ __attribute__((aligned(16))) float lds[2 * BUF];            // K (sweep 1) / V (sweep 2) tiles
+    // K (sweep 1) / V (sweep 2) tiles, double-buffered.  The two buffers are
+    // separate arrays and every access names its array statically (loops are
+    // unrolled by two), so the compiler can tell a direct load into one buffer
+    // from reads of the other and inserts no wait of its own between them.
+    __shared__ __attribute__((aligned(16))) float lds0[BUF];
+    __shared__ __attribute__((aligned(16))) float lds1[BUF];
     __shared__ __attribute__((aligned(16))) float sbuf[kWaves * kTileElems];  // each wave's next score tile
 
     const int tid = threadIdx.x;
@@ -96,13 +101,12 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
             *(f32x4*)(tiles + (size_t)kt_t * kTileElems + p * 256 + lane * 4) = x;
         }
     };
-    LT::load(lds, Kp, 0, T, tid);
+    LT::load(lds0, Kp, 0, T, tid);
     wait_vmcnt<0>();
     __syncthreads();
     f32x16 accp = {};
-    for (int kt = 0; kt <= kt_end; ++kt) {
-        const float* cur = lds + (kt & 1) * BUF;
-        if (kt < kt_end) LT::load(lds + ((kt + 1) & 1) * BUF, Kp, (kt + 1) * kTile, T, tid);
+    auto sweep1 = [&](int kt, const float* cur, float* nxt) __attribute__((always_inline)) {
+        if (kt < kt_end) LT::load(nxt, Kp, (kt + 1) * kTile, T, tid);
         const bool stores = active && kt <= qt && kt > 0;
         if (active && kt <= qt) {
             f32x4 xk[D / 8];
@@ -122,7 +126,11 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
         // the K tile loads were issued first; the 4 score stores may stay in flight
         if (stores) wait_vmcnt<4>();
         else wait_vmcnt<0>();
-        __syncthreads();
+        lds_barrier();
+    };
+    for (int kt = 0; kt <= kt_end; kt += 2) {
+        sweep1(kt, lds0, lds1);
+        if (kt + 1 <= kt_end) sweep1(kt + 1, lds1, lds0);
     }
     if (active) {
 #pragma unroll
@@ -174,7 +182,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
         }
     };
 
-    LT::load(lds, V, 0, T, tid);
+    LT::load(lds0, V, 0, T, tid);
     if (active) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
@@ -195,9 +203,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
     }
     wait_vmcnt<0>();
     __syncthreads();
-    for (int kt = 0; kt <= kt_end; ++kt) {
-        const float* cur = lds + (kt & 1) * BUF;
-        if (kt < kt_end) LT::load(lds + ((kt + 1) & 1) * BUF, V, (kt + 1) * kTile, T, tid);
+    auto sweep2 = [&](int kt, const float* cur, float* nxt) __attribute__((always_inline)) {
+        if (kt < kt_end) LT::load(nxt, V, (kt + 1) * kTile, T, tid);
         const bool more = active && kt + 1 <= qt;      // tile kt+1 exists for this wave
         const bool prefetch = active && kt + 2 <= qt;  // and tile kt+2
         if (active && kt <= qt) {
@@ -236,7 +243,11 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
         // the V tile loads were issued first; the score prefetch may stay in flight
         if (prefetch) wait_vmcnt<4>();
         else wait_vmcnt<0>();
-        __syncthreads();
+        lds_barrier();
+    };
+    for (int kt = 0; kt <= kt_end; kt += 2) {
+        sweep2(kt, lds0, lds1);
+        if (kt + 1 <= kt_end) sweep2(kt + 1, lds1, lds0);
     }
     W += __shfl_xor(W, 32);
     if (REC == REC_NEAREST) WL += __shfl_xor(WL, 32);
