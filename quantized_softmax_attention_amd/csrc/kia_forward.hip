@@ -69,59 +69,72 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
 
     // ---- sweep 1: scores, row extremes --------------------------------------
     // K tiles arrive by direct global -> LDS loads one tile ahead.  Per wave
-    // the matrix instructions of key tile kt interleave with the extreme
-    // tracking and the score store of tile kt-1.  Each lane walks its keys in
-    // increasing order, so a strict comparison keeps the lowest index among
-    // equal extremes.  Only a wave's last tile (the diagonal) needs the causal
-    // mask; lanes past the end of the sequence compute values never stored as
-    // results.
+    // the matrix instructions of key tile kt interleave with the store and the
+    // extreme tracking of tile kt-1.  Tracking is per tile: each lane keeps its
+    // running max / min and the first tile where a strictly larger (smaller)
+    // value appeared; the key index inside that tile is looked up once at the
+    // end, so the lowest index among equal extremes is kept.  Only a wave's
+    // last tile (the diagonal) needs the causal mask; lanes past the end of the
+    // sequence compute values never stored as results.
     float m = -INFINITY, n = INFINITY;
-    int am = 0, an = 0;
-    auto track = [&](const f32x16& acc, int kt_t, auto diag_t, int r) {
-        constexpr bool DIAG = decltype(diag_t)::value;
-        const int key = kt_t * kTile + acc_row(r, hl);
-        const float sc = acc[r];
-        const bool valid = DIAG ? key <= qrow : true;
-        const bool gt = valid && sc > m;
-        m = gt ? sc : m;
-        am = gt ? key : am;
-        if (CAL == CAL_MINMAX) {
-            const bool lt = valid && sc < n;
-            n = lt ? sc : n;
-            an = lt ? key : an;
-        }
-        if ((r & 3) == 3) {
-            const int p = r >> 2;
+    int amt = 0, ant = 0;  // tile of the first occurrence of this lane's extremes
+    int am = 0, an = 0;    // row argmax / argmin (lowest key index)
+    auto store_tile = [&](const f32x16& acc, int kt_t, bool diag) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
             f32x4 x;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const bool ok = DIAG ? (kt_t * kTile + acc_row(4 * p + j, hl)) <= qrow : true;
+                const bool ok = !diag || (kt_t * kTile + acc_row(4 * p + j, hl)) <= qrow;
                 x[j] = ok ? acc[4 * p + j] : 0.f;
             }
             *(f32x4*)(tiles + (size_t)kt_t * kTileElems + p * 256 + lane * 4) = x;
         }
     };
+    auto track_tile = [&](const f32x16& acc, int kt_t, bool diag) {
+        float x[16], y[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const bool ok = !diag || (kt_t * kTile + acc_row(r, hl)) <= qrow;
+            x[r] = ok ? acc[r] : -INFINITY;
+            y[r] = ok ? acc[r] : INFINITY;
+        }
+        float mt = x[0], nt = y[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) {
+            mt = fmaxf(mt, x[r]);
+            if (CAL == CAL_MINMAX) nt = fminf(nt, y[r]);
+        }
+        const bool up = mt > m;
+        amt = up ? kt_t : amt;
+        m = up ? mt : m;
+        if (CAL == CAL_MINMAX) {
+            const bool dn = nt < n;
+            ant = dn ? kt_t : ant;
+            n = dn ? nt : n;
+        }
+    };
     LT::load(lds0, Kp, 0, T, tid);
     wait_vmcnt<0>();
     __syncthreads();
-    f32x16 accp = {};
-    auto sweep1 = [&](int kt, const float* cur, float* nxt) __attribute__((always_inline)) {
+    f32x16 accA = {}, accB = {};
+    // key tile kt: MFMAs into acc, store + track the previous tile held in prv
+    auto sweep1 = [&](int kt, const float* cur, float* nxt, f32x16& acc, const f32x16& prv)
+        __attribute__((always_inline)) {
         if (kt < kt_end) LT::load(nxt, Kp, (kt + 1) * kTile, T, tid);
         const bool stores = active && kt <= qt && kt > 0;
         if (active && kt <= qt) {
             f32x4 xk[D / 8];
 #pragma unroll
             for (int p = 0; p < D / 8; ++p) xk[p] = *(const f32x4*)(cur + LT::off(li, 8 * p + 4 * hl));
-            f32x16 acc = {};
-            auto mstep = [&](int s) { acc = mfma32x32x2(xk[s >> 2][s & 3], qf[s], acc); };
+            acc = f32x16{};
             if (kt > 0) {
-                interleave<D / 2, 16>(mstep, [&](int r) { track(accp, kt - 1, std::false_type{}, r); });
-                pin_interleave<D / 2, 4, D / 8>();
-            } else {
-#pragma unroll
-                for (int s = 0; s < D / 2; ++s) mstep(s);
+                store_tile(prv, kt - 1, false);
+                track_tile(prv, kt - 1, false);
             }
-            accp = acc;
+#pragma unroll
+            for (int s = 0; s < D / 2; ++s) acc = mfma32x32x2(xk[s >> 2][s & 3], qf[s], acc);
+            if (kt > 0) pin_interleave<D / 2, 1, D / 8>();
         }
         // the K tile loads were issued first; the 4 score stores may stay in flight
         if (stores) wait_vmcnt<4>();
@@ -129,22 +142,48 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
         lds_barrier();
     };
     for (int kt = 0; kt <= kt_end; kt += 2) {
-        sweep1(kt, lds0, lds1);
-        if (kt + 1 <= kt_end) sweep1(kt + 1, lds1, lds0);
+        sweep1(kt, lds0, lds1, accA, accB);
+        if (kt + 1 <= kt_end) sweep1(kt + 1, lds1, lds0, accB, accA);
     }
     if (active) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) track(accp, qt, std::true_type{}, r);
+        // the diagonal tile qt sits in accA for even qt, accB for odd
+        if (qt & 1) { store_tile(accB, qt, true); track_tile(accB, qt, true); }
+        else { store_tile(accA, qt, true); track_tile(accA, qt, true); }
     }
-    // the two lane halves of a query saw disjoint keys: merge, lowest index on ties
+    // Row extremes: the two lane halves of a query saw disjoint keys.  Each
+    // half whose extreme equals the row's reads back its 16 stored scores of
+    // the tile where that extreme first appeared and takes the first key
+    // attaining it; the smaller key of the two halves wins.  (The wave's own
+    // score stores precede these loads, so they see the stored values; masked
+    // diagonal entries are excluded by the causal test.)
     {
-        const float mo = __shfl_xor(m, 32);
-        const int ao = __shfl_xor(am, 32);
-        if (mo > m || (mo == m && ao < am)) { m = mo; am = ao; }
+        const float M = fmaxf(m, __shfl_xor(m, 32));
+        const float N = (CAL == CAL_MINMAX) ? fminf(n, __shfl_xor(n, 32)) : 0.f;
+        int ia = 0x7fffffff, ib = 0x7fffffff;
+        if (active) {
+            f32x4 xa[4], xb[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) xa[p] = *(const f32x4*)(tiles + (size_t)amt * kTileElems + p * 256 + lane * 4);
+            if (CAL == CAL_MINMAX) {
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+                    xb[p] = *(const f32x4*)(tiles + (size_t)ant * kTileElems + p * 256 + lane * 4);
+            }
+#pragma unroll
+            for (int r = 15; r >= 0; --r) {
+                const int ka = amt * kTile + acc_row(r, hl);
+                if (m == M && ka <= qrow && xa[r >> 2][r & 3] == M) ia = ka;
+                if (CAL == CAL_MINMAX) {
+                    const int kb = ant * kTile + acc_row(r, hl);
+                    if (n == N && kb <= qrow && xb[r >> 2][r & 3] == N) ib = kb;
+                }
+            }
+        }
+        m = M;
+        am = min(ia, __shfl_xor(ia, 32));
         if (CAL == CAL_MINMAX) {
-            const float no = __shfl_xor(n, 32);
-            const int bo = __shfl_xor(an, 32);
-            if (no < n || (no == n && bo < an)) { n = no; an = bo; }
+            n = N;
+            an = min(ib, __shfl_xor(ib, 32));
         }
     }
     if (!qvalid) { m = 0.f; n = 0.f; }
@@ -154,7 +193,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
     // V tiles arrive like the K tiles; each wave's next score tile arrives by a
     // direct load into its LDS slot.  Per wave the matrix instructions of
     // tile kt (weights already computed) interleave with the reconstruction of
-    // tile kt+1.
+    // tile kt+1; the two unrolled halves swap weight registers.
     float W = 0.f, WL = 0.f;
     f32x16 oacc[NB];
     f32x16 olacc[PROB ? NB : 1];
@@ -163,21 +202,27 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
 #pragma unroll
     for (int b = 0; b < (PROB ? NB : 1); ++b) olacc[b] = f32x16{};
 
-    float sv[16], w[16], wl[16], wn[16], wln[16];
-    auto recon = [&](int kt_t, auto diag_t, int r) {
+    float sv[16], wA[16], wlA[PROB ? 16 : 1], wB[16], wlB[PROB ? 16 : 1];
+    auto recon = [&](int kt_t, auto diag_t, int r, float* w, float* wl) {
         constexpr bool DIAG = decltype(diag_t)::value;
         const int key = kt_t * kTile + acc_row(r, hl);
         const bool valid = DIAG ? key <= qrow : true;
-        const Recon e = reconstruct<CAL, REC == REC_NEAREST>(rg, sv[r]);
-        const bool keep = valid && e.inwin;
-        const float wh = (REC == REC_LERP) ? e.wl : e.wn;
-        wn[r] = keep ? wh : 0.f;
-        W += wn[r];
-        wln[r] = keep ? e.wl : 0.f;
-        if (REC == REC_NEAREST) WL += wln[r];
+        const float s = sv[r];
+        const float u = (rg.m - s) * rg.invh;
+        const bool keep = valid && ((CAL == CAL_MINMAX) ? true : (u <= rg.Kf));
+        // unclamped segment: at u = K (the row min) the LERP value is g_K either way
+        const float fi = floorf(u);
+        const float g = fast_exp2(-fi * rg.hl2);
+        const float wlv = g * fmaf(fi - u, rg.c, 1.f);
+        float wv = wlv;
+        if (REC == REC_NEAREST) wv = fast_exp2(-floorf(u + 0.5f) * rg.hl2);
+        w[r] = keep ? wv : 0.f;
+        W += w[r];
+        if (REC == REC_NEAREST) WL += keep ? wlv : 0.f;
+        if (PROB) wl[r] = keep ? wlv : 0.f;
         if (DUMP && qvalid && valid) {
-            int idx = (REC == REC_LERP) ? (int)e.fi : (int)floorf(e.u + 0.5f);
-            if (!e.inwin) idx = -1;
+            int idx = (REC == REC_LERP) ? (int)fminf(fi, rg.Kf - 1.f) : (int)floorf(u + 0.5f);
+            if (!keep) idx = -1;
             a.idx_dump[((size_t)bh * T + qrow) * T + key] = idx;
         }
     };
@@ -193,17 +238,17 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
         if (qt > 0) dma_tile(sw, tiles + kTileElems, lane);
         if (qt == 0) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) recon(0, std::true_type{}, r);
+            for (int r = 0; r < 16; ++r) recon(0, std::true_type{}, r, wA, wlA);
         } else {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) recon(0, std::false_type{}, r);
+            for (int r = 0; r < 16; ++r) recon(0, std::false_type{}, r, wA, wlA);
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) { w[r] = wn[r]; wl[r] = wln[r]; }
     }
     wait_vmcnt<0>();
     __syncthreads();
-    auto sweep2 = [&](int kt, const float* cur, float* nxt) __attribute__((always_inline)) {
+    // tile kt: weights in (w, wl); reconstruct tile kt+1 into (wn, wln)
+    auto sweep2 = [&](int kt, const float* cur, float* nxt, const float* w, const float* wl, float* wn, float* wln)
+        __attribute__((always_inline)) {
         if (kt < kt_end) LT::load(nxt, V, (kt + 1) * kTile, T, tid);
         const bool more = active && kt + 1 <= qt;      // tile kt+1 exists for this wave
         const bool prefetch = active && kt + 2 <= qt;  // and tile kt+2
@@ -228,17 +273,15 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
                 if (PROB) olacc[b] = mfma32x32x2(xv[s], wl[kk], olacc[b]);
             };
             if (kt + 1 < qt) {
-                interleave<16 * NB, 16>(mstep, [&](int r) { recon(kt + 1, std::false_type{}, r); });
+                interleave<16 * NB, 16>(mstep, [&](int r) { recon(kt + 1, std::false_type{}, r, wn, wln); });
                 pin_interleave<16 * NB, (PROB ? 4 : 6) * 2 / NB, 16 * NB>();
             } else if (kt + 1 == qt) {
-                interleave<16 * NB, 16>(mstep, [&](int r) { recon(kt + 1, std::true_type{}, r); });
+                interleave<16 * NB, 16>(mstep, [&](int r) { recon(kt + 1, std::true_type{}, r, wn, wln); });
                 pin_interleave<16 * NB, (PROB ? 4 : 6) * 2 / NB, 16 * NB>();
             } else {
 #pragma unroll
                 for (int s = 0; s < 16 * NB; ++s) mstep(s);
             }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) { w[r] = wn[r]; wl[r] = wln[r]; }
         }
         // the V tile loads were issued first; the score prefetch may stay in flight
         if (prefetch) wait_vmcnt<4>();
@@ -246,8 +289,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
         lds_barrier();
     };
     for (int kt = 0; kt <= kt_end; kt += 2) {
-        sweep2(kt, lds0, lds1);
-        if (kt + 1 <= kt_end) sweep2(kt + 1, lds1, lds0);
+        sweep2(kt, lds0, lds1, wA, wlA, wB, wlB);
+        if (kt + 1 <= kt_end) sweep2(kt + 1, lds1, lds0, wB, wlB, wA, wlA);
     }
     W += __shfl_xor(W, 32);
     if (REC == REC_NEAREST) WL += __shfl_xor(WL, 32);
