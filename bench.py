@@ -127,6 +127,7 @@ def cpu_baseline(wname, variant, n_slices, flop_per_slice):
     import multiprocessing as mp
     from workloads import WORKLOADS
     w = WORKLOADS[wname]
+    n_slices = max(1, min(n_slices, w.B * w.H))
     cores = max(1, min(len(os.sched_getaffinity(0)), 16, n_slices))
     slices = [(wname, variant, i // w.H % w.B, i % w.H) for i in range(n_slices)]
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
@@ -148,6 +149,80 @@ def cpu_baseline(wname, variant, n_slices, flop_per_slice):
     }
 
 
+def _find_csv(d, suffix):
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError(f"no *{suffix} under {d}")
+
+
+def _counter_means(d, counter):
+    """Mean value of one counter per kernel name in a rocprofv3 --pmc csv run."""
+    import csv
+    acc = {}
+    for r in csv.DictReader(open(_find_csv(d, "counter_collection.csv"))):
+        if r["Counter_Name"] != counter:
+            continue
+        acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def _kernel_key(name):
+    for key, pat in (("forward", "kia_forward_kernel"), ("backward_rows", "kia_backward_rows_kernel"),
+                     ("backward_cols", "kia_backward_cols_kernel")):
+        if pat in name:
+            return key
+    return None
+
+
+def ingest_pmc(args):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the three kernels, scaled by what the same
+    counters read for a plain device copy of known size, into bytes per launch."""
+    d = args.ingest_pmc
+    copy_bytes = args.copy_calib * (1 << 20) if args.copy_calib else 1 << 30
+    cf = [v for k, v in _counter_means(os.path.join(d, "copy_fetch"), "FETCH_SIZE").items() if "copy" in k.lower()]
+    cw = [v for k, v in _counter_means(os.path.join(d, "copy_write"), "WRITE_SIZE").items() if "copy" in k.lower()]
+    f_scale = copy_bytes / (max(cf) * 1024.0)
+    w_scale = copy_bytes / (max(cw) * 1024.0)
+    fetch = _counter_means(os.path.join(d, "fetch"), "FETCH_SIZE")
+    write = _counter_means(os.path.join(d, "write"), "WRITE_SIZE")
+    variant = dict(DEFAULT_VARIANT[args.workload])
+    for key in ("K", "calibration", "reconstruction", "surrogate", "grad_rule"):
+        if getattr(args, key) is not None:
+            variant[key] = getattr(args, key)
+    kernels = {}
+    for name, kib in fetch.items():
+        key = _kernel_key(name)
+        if key is None:
+            continue
+        wk = next((v for n, v in write.items() if _kernel_key(n) == key), 0.0)
+        fb, wb = kib * 1024.0 * f_scale, wk * 1024.0 * w_scale
+        kernels[key] = {"kernel_name": name, "fetch_kib_raw": round(kib, 1), "write_kib_raw": round(wk, 1),
+                        "fetch_bytes": int(fb), "write_bytes": int(wb), "hbm_bytes_per_launch": int(fb + wb)}
+    out = {"workload": args.workload, "variant": variant, "source_digest": source_digest(),
+           "copy_calibration": {"bytes_each_way": copy_bytes, "fetch_scale": round(f_scale, 4),
+                                "write_scale": round(w_scale, 4)},
+           "kernels": kernels}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
+def summarize_trace(d):
+    import csv
+    rows = list(csv.DictReader(open(_find_csv(d, "kernel_stats.csv"))))
+    lines = ["| kernel | calls | avg (us) | min (us) | max (us) | total (ms) | share |", "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"]
+        lines.append(f"| `{name[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.1f}% |")
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -159,11 +234,23 @@ def main():
     ap.add_argument("--reconstruction", choices=["lerp", "nearest"])
     ap.add_argument("--surrogate", choices=["weight", "prob"])
     ap.add_argument("--grad-rule", dest="grad_rule", choices=["full", "detach", "max_only", "min_only"])
-    ap.add_argument("--cpu-slices", type=int, default=32, help="oracle sample size for the CPU baseline")
+    ap.add_argument("--cpu-slices", type=int, default=96,
+                    help="oracle sample size for the CPU baseline, in (b, h) slices (capped at B*H)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--ingest-pmc", metavar="DIR",
+                    help="host only: turn rocprofv3 counter passes under DIR (fetch/, write/, copy_fetch/, "
+                         "copy_write/) into profiles/traffic.json and a text summary")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="host only: print a markdown summary of a rocprofv3 --kernel-trace --stats run")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(args)
+        return
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: K-interval attention shards by (batch, head) slice with no "
