@@ -101,7 +101,14 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
     // a row with a single causal key has P = 1 whatever its score: zero gradient
     const float invWe = (qrow == 0) ? 0.f : ((REC == REC_NEAREST && PROB) ? 1.f / WL : invW);
 
-    float SA = 0.f, SB = 0.f;  // row sums of the direct term and of dL/dw * Wd (Wd = g * t)
+    // Row sums of the direct term (SA) and of dL/dw * Wd (SB, Wd = g * t).
+    // SA is summed per tile in fp32 (in key order, no contraction, so the
+    // epilogue can reproduce a tile's partial bit for bit) and across tiles
+    // with a compensated (hi, lo) pair.  SB / K enters the two routed terms
+    // with opposite signs and cancels exactly, so an fp32 running sum
+    // suffices for it.
+    float SA = 0.f, SB = 0.f;
+    float SAhi = 0.f, SAlo = 0.f;  // compensated running sum of the per-tile SA
     f32x16 dq[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) dq[b] = f32x16{};
@@ -153,6 +160,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
 
             float ds[16], pr[16];
             auto grads = [&](auto diag_t) {
+                // no contraction: SA must sum exactly the rounded dS values that are
+                // stored, or the routed calibration terms stop cancelling them
+#pragma clang fp contract(off)
                 constexpr bool DIAG = decltype(diag_t)::value;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -198,6 +208,13 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
                 const int b = s2 >> 4, kk = s2 & 15;
                 dq[b] = mfma32x32x2(xk[s2], ds[kk], dq[b]);
             }
+            {   // error-free addition of the tile's sum (Knuth's TwoSum)
+                const float sum = SAhi + SA;
+                const float bv = sum - SAhi;
+                SAlo += (SAhi - (sum - bv)) + (SA - bv);
+                SAhi = sum;
+                SA = 0.f;
+            }
         }
         // the staging loads were issued first; the score prefetch (4) and the
         // P / dS stores (8) may stay in flight
@@ -210,27 +227,55 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
         lds_barrier();
     }
 
-    SA += __shfl_xor(SA, 32);
     SB += __shfl_xor(SB, 32);
-    float Cm, Cn;
-    if (CAL == CAL_MINMAX) {
-        Cm = -SA + SB / rg.Kf;
-        Cn = -SB / rg.Kf;
-    } else {
-        Cm = -SA;
-        Cn = 0.f;
-    }
-    if (rg.degen) { Cm = 0.f; Cn = 0.f; }
-    const bool use_max = (a.rule == GRAD_FULL || a.rule == GRAD_MAX_ONLY);
-    const bool use_min = CAL == CAL_MINMAX && (a.rule == GRAD_FULL || a.rule == GRAD_MIN_ONLY);
-    const float cm = use_max ? Cm : 0.f;
-    const float cn = use_min ? Cn : 0.f;
+    const bool use_max = !rg.degen && (a.rule == GRAD_FULL || a.rule == GRAD_MAX_ONLY);
+    const bool use_min = !rg.degen && CAL == CAL_MINMAX && (a.rule == GRAD_FULL || a.rule == GRAD_MIN_ONLY);
+    // causal key indices by construction; clamped so no stats value can address outside the row
+    const int ka = min(max(qvalid ? a.row_a[ri] : 0, 0), max(qrow, 0));
+    const int kb = min(max(qvalid ? a.row_b[ri] : 0, 0), max(qrow, 0));
 
-    // the wave's dS tile stores must be visible before it updates two entries per row
+    // the wave's dS tile stores must be visible before it reads and updates them
     __threadfence_block();
+
+    // The argmax entry receives C_m = -SA + SB/K (MinMax) or -SA (FWM), so its
+    // final value is minus the other keys' direct terms (plus SB/K).  Where P
+    // is saturated the argmax's own direct term is the fp32 noise of
+    // dP - delta, far above the row's true gradient, and adding C_m to it would
+    // cancel that noise only to its rounding.  So the final value is formed
+    // from the other keys alone: the lane half holding key a re-reads its 16
+    // entries of that tile, reproduces the tile's partial sum bit for bit and
+    // replaces it by the partial without key a.
+    // (The noisy partial is taken out of hi first, which is exact, so no
+    // intermediate carries its magnitude into the fp64 rounding.)
+    double sa_lane = (double)SAhi + (double)SAlo;
+    const float* ta = dstiles + (size_t)(ka >> 5) * kTileElems;
+    const int kra = ka & 31;
+    if (qvalid && use_max && ((kra >> 2) & 1) == hl) {
+        float p_all = 0.f, p_ex = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int kk = acc_row(r, hl);
+            const float x = ta[kmajor_offset(li, kk)];
+            p_all += x;
+            p_ex += (kk == kra) ? 0.f : x;
+        }
+        sa_lane = (((double)SAhi - (double)p_all) + (double)SAlo) + (double)p_ex;
+    }
+    const double sa_excl = sa_lane + __shfl_xor(sa_lane, 32);
+    double sbk = 0.0;
+    if (CAL == CAL_MINMAX) sbk = (double)(SB / rg.Kf);
+    const float cn = use_min ? (float)(-sbk) : 0.f;
+
     if (qvalid) {
-        const int ka = a.row_a[ri];
-        const int kb = a.row_b[ri];
+        float cm = 0.f;
+        if (use_max) {
+            // both lane halves read the loop's direct term; the first writes the final value
+            float* e = dstiles + (size_t)(ka >> 5) * kTileElems + kmajor_offset(li, kra);
+            const float old = *e;
+            const float fin = (float)(sbk - sa_excl);
+            cm = fin - old;  // the routed C_m, as applied on top of the loop's direct term
+            if (hl == 0) *e = fin;
+        }
         float* dqrow = a.dq + head + (size_t)qrow * D;
 #pragma unroll
         for (int b = 0; b < NB; ++b)
@@ -247,12 +292,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
         if (hl == 0) {
             a.row_cm[ri] = cm;
             a.row_cn[ri] = cn;
-            // fold the routed calibration terms into the row's dS (argmax != argmin
-            // whenever they are non-zero, so the two updates never meet)
-            if (cm != 0.f) {
-                float* e = dstiles + (size_t)(ka >> 5) * kTileElems + kmajor_offset(li, ka & 31);
-                *e += cm;
-            }
+            // argmax != argmin whenever C_n is routed (non-degenerate rows)
             if (cn != 0.f) {
                 float* e = dstiles + (size_t)(kb >> 5) * kTileElems + kmajor_offset(li, kb & 31);
                 *e += cn;

@@ -179,11 +179,14 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
                 }
             }
         }
+        // a row with no finite extreme (NaN scores) finds no key: fall back to key 0
         m = M;
         am = min(ia, __shfl_xor(ia, 32));
+        if (am == 0x7fffffff) am = 0;
         if (CAL == CAL_MINMAX) {
             n = N;
             an = min(ib, __shfl_xor(ib, 32));
+            if (an == 0x7fffffff) an = 0;
         }
     }
     if (!qvalid) { m = 0.f; n = 0.f; }
@@ -194,7 +197,18 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
     // direct load into its LDS slot.  Per wave the matrix instructions of
     // tile kt (weights already computed) interleave with the reconstruction of
     // tile kt+1; the two unrolled halves swap weight registers.
-    float W = 0.f, WL = 0.f;
+    // Normalisers: each tile's 16 weights are summed in fp32, the tile sums in
+    // fp64, so the rounding error stays at ~16 ulp of W for rows of any length.
+    float Wt = 0.f, WLt = 0.f;
+    double W64 = 0.0, WL64 = 0.0;
+    auto flush_sums = [&]() {
+        W64 += (double)Wt;
+        Wt = 0.f;
+        if (REC == REC_NEAREST) {
+            WL64 += (double)WLt;
+            WLt = 0.f;
+        }
+    };
     f32x16 oacc[NB];
     f32x16 olacc[PROB ? NB : 1];
 #pragma unroll
@@ -204,6 +218,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
 
     float sv[16], wA[16], wlA[PROB ? 16 : 1], wB[16], wlB[PROB ? 16 : 1];
     auto recon = [&](int kt_t, auto diag_t, int r, float* w, float* wl) {
+        // no contraction: every instantiation (with or without the Prob-STE
+        // extras) rounds the weights and their sums identically
+#pragma clang fp contract(off)
         constexpr bool DIAG = decltype(diag_t)::value;
         const int key = kt_t * kTile + acc_row(r, hl);
         const bool valid = DIAG ? key <= qrow : true;
@@ -217,8 +234,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
         float wv = wlv;
         if (REC == REC_NEAREST) wv = fast_exp2(-floorf(u + 0.5f) * rg.hl2);
         w[r] = keep ? wv : 0.f;
-        W += w[r];
-        if (REC == REC_NEAREST) WL += keep ? wlv : 0.f;
+        Wt += w[r];
+        if (REC == REC_NEAREST) WLt += keep ? wlv : 0.f;
         if (PROB) wl[r] = keep ? wlv : 0.f;
         if (DUMP && qvalid && valid) {
             int idx = (REC == REC_LERP) ? (int)fminf(fi, rg.Kf - 1.f) : (int)floorf(u + 0.5f);
@@ -243,6 +260,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
 #pragma unroll
             for (int r = 0; r < 16; ++r) recon(0, std::false_type{}, r, wA, wlA);
         }
+        flush_sums();
     }
     wait_vmcnt<0>();
     __syncthreads();
@@ -283,6 +301,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
                 for (int s = 0; s < 16 * NB; ++s) mstep(s);
             }
         }
+        flush_sums();
         // the V tile loads were issued first; the score prefetch may stay in flight
         if (prefetch) wait_vmcnt<4>();
         else wait_vmcnt<0>();
@@ -292,9 +311,13 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
         sweep2(kt, lds0, lds1, wA, wlA, wB, wlB);
         if (kt + 1 <= kt_end) sweep2(kt + 1, lds1, lds0, wB, wlB, wA, wlA);
     }
-    W += __shfl_xor(W, 32);
-    if (REC == REC_NEAREST) WL += __shfl_xor(WL, 32);
-    else WL = W;  // LERP: the forward weights are the LERP weights
+    W64 += __shfl_xor(W64, 32);
+    const float W = (float)W64;
+    float WL = W;  // LERP: the forward weights are the LERP weights
+    if (REC == REC_NEAREST) {
+        WL64 += __shfl_xor(WL64, 32);
+        WL = (float)WL64;
+    }
 
     if (qvalid) {
         const float invW = 1.f / W;

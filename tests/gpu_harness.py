@@ -74,9 +74,23 @@ def run_gpu(q, k, v, do, params, want_dense=True, want_idx=True):
     return out
 
 
-def gpu_slice(gpu, b, h):
-    """numpy copies of every per-slice entry of a run_gpu result."""
-    return {key: val[b, h].cpu().numpy() for key, val in gpu.items() if not key.startswith("_")}
+def gpu_slice(gpu, b, h, rows=None):
+    """numpy copies of every per-slice entry of a run_gpu result; the [T, T]
+    entries only for the rows asked for (other rows left zero)."""
+    out = {}
+    for key, val in gpu.items():
+        if key.startswith("_"):
+            continue
+        x = val[b, h]
+        if rows is not None and x.dim() == 2 and x.shape[0] == x.shape[1]:
+            import torch
+            idx = torch.as_tensor(rows, device=x.device)
+            dense = np.zeros(tuple(x.shape), dtype=np.int32 if x.dtype == torch.int32 else np.float32)
+            dense[rows] = x.index_select(0, idx).cpu().numpy()
+            out[key] = dense
+        else:
+            out[key] = x.cpu().numpy()
+    return out
 
 
 def score_bound(Qh, Kh):
@@ -88,18 +102,53 @@ def score_bound(Qh, Kh):
     return (d + 3) * 2.0 ** -24 * absdot
 
 
-class SliceCheck:
-    """Oracle for one (b, h) slice plus the ambiguity analysis against the GPU's run."""
+def partial_head_backward(Qh, Kh, Vh, dOh, p_or, rows, tail):
+    """The oracle's per-row forward + backward for the rows asked for, with dK
+    and dV accumulated over the rows t >= tail only: exact for keys >= tail
+    (every row that reaches such a key is >= tail), so long sequences can be
+    checked on their last keys without the whole quadratic slice."""
+    T, d = Qh.shape
+    scale = 1.0 / np.sqrt(d)
+    Q64, K64, V64, dO64 = (x.astype(np.float64) for x in (Qh, Kh, Vh, dOh))
+    dQ = np.full((T, d), np.nan)
+    dK = np.zeros((T, d))
+    dV = np.zeros((T, d))
+    recs = {}
+    for t in sorted(set(rows) | set(range(tail, T))):
+        s = O.row_scores(Q64[t], K64[: t + 1])
+        fw = O.row_forward(s, p_or)
+        bw = O.row_backward(fw, V64[: t + 1] @ dO64[t], p_or)
+        dQ[t] = (bw.dS @ K64[: t + 1]) * scale
+        if t >= tail:
+            dK[tail: t + 1] += np.outer(bw.dS[tail:], Q64[t]) * scale
+            dV[tail: t + 1] += np.outer(fw.P[tail:], dO64[t])
+        recs[t] = (fw, bw)
+    return {"dQ": dQ, "dK": dK, "dV": dV, "rows": recs}
 
-    def __init__(self, q, k, v, do, p_or, gpu, b, h):
+
+class SliceCheck:
+    """Oracle for one (b, h) slice plus the ambiguity analysis against the GPU's run.
+
+    rows=None checks the whole slice.  Otherwise only the listed rows and the
+    rows t >= tail are recomputed; O and dQ are compared on those rows and dK,
+    dV on the keys >= tail."""
+
+    def __init__(self, q, k, v, do, p_or, gpu, b, h, rows=None, tail=None):
         self.p = p_or
         Qh, Kh, Vh, dOh = q[b, h], k[b, h], v[b, h], do[b, h]
         self.T, self.d = Qh.shape
-        self.ref = O.head_backward(Qh, Kh, Vh, dOh, p_or, keep_rows=True)
-        self.O_ref = np.stack([self.ref["rows"][t][0].P @ Vh[: t + 1].astype(np.float64)
-                               for t in range(self.T)])
-        self.g = gpu_slice(gpu, b, h)
-        self.sb = score_bound(Qh, Kh)
+        if rows is None:
+            self.ref = O.head_backward(Qh, Kh, Vh, dOh, p_or, keep_rows=True)
+            self.tail = 0
+        else:
+            self.tail = self.T if tail is None else tail
+            self.ref = partial_head_backward(Qh, Kh, Vh, dOh, p_or, rows, self.tail)
+        self.rows = sorted(self.ref["rows"])
+        self.O_ref = np.full((self.T, self.d), np.nan)
+        for t in self.rows:
+            self.O_ref[t] = self.ref["rows"][t][0].P @ Vh[: t + 1].astype(np.float64)
+        self.g = gpu_slice(gpu, b, h, self.rows)
+        self.sb = {t: score_bound(Qh[t: t + 1], Kh[: t + 1])[0] for t in self.rows}
         self._analyse()
 
     def _analyse(self):
@@ -113,13 +162,13 @@ class SliceCheck:
         self.n_amb_pairs = 0
         self.idx_mismatch = 0
         self.idx_checked = 0
-        for t in range(T):
+        for t in self.rows:
             fw, bw = self.ref["rows"][t]
             s_ref = fw.s
             cal = fw.cal
             sg = g["S"][t, : t + 1].astype(np.float64) if "S" in g else None
             if sg is not None:
-                viol = np.abs(sg - s_ref) > self.sb[t, : t + 1] * 1.0 + 1e-30
+                viol = np.abs(sg - s_ref) > self.sb[t] * 1.0 + 1e-30
                 self.score_viol += int(viol.sum())
             # argmax / argmin near ties
             ds_obs = np.abs(sg - s_ref).max() if sg is not None else 0.0
@@ -197,7 +246,12 @@ class SliceCheck:
         T = self.T
         ref = {"O": self.O_ref, "dQ": self.ref["dQ"], "dK": self.ref["dK"], "dV": self.ref["dV"]}[name]
         got = self.g[name].astype(np.float64)
-        keep = np.ones(T, dtype=bool)
+        keep = np.zeros(T, dtype=bool)
+        if name in ("O", "dQ"):
+            keep[self.rows] = True
+        else:
+            keep[self.tail:] = True
+        region = keep.copy()                 # entries this check covers, before exclusions
         if name == "O":
             keep &= ~self.amb_fwd
         elif name == "dQ":
@@ -207,7 +261,7 @@ class SliceCheck:
                 keep[list(self.amb_keys_bwd)] = False
             for t, _ in self.fwd_unstable_rows:
                 keep[: t + 1] = False
-        scale = np.abs(ref).max()
+        scale = np.abs(ref[region]).max() if region.any() else 0.0
         if scale == 0:
             return 0.0, int(keep.sum())
         err = np.abs(got[keep] - ref[keep]).max() / scale if keep.any() else 0.0
@@ -225,7 +279,7 @@ class SliceCheck:
         g = self.g
         Vh, dOh = v[b, h].astype(np.float64), do[b, h].astype(np.float64)
         bad = []
-        for t in range(self.T):
+        for t in self.rows:
             row = g["dS"][t, : t + 1].astype(np.float64)
             l1 = np.abs(row).sum()
             floor = 0.0
