@@ -101,7 +101,8 @@ def _oracle_slice(args):
     cal = {"minmax": O.MINMAX, "fwm": O.FWM}[variant["calibration"]]
     rec = {"lerp": O.LERP, "nearest": O.NEAREST}[variant["reconstruction"]]
     ste = {"weight": O.WEIGHT_STE, "prob": O.PROB_STE}[variant["surrogate"]]
-    rule = {"full": O.FULL, "detach": O.DETACH, "max_only": O.MAX_ONLY, "min_only": O.MIN_ONLY}[variant["grad_rule"]]
+    rule = {"full": O.FULL, "detach": O.DETACH, "max_only": O.MAX_ONLY, "min_only": O.MIN_ONLY,
+            "p1": O.P1}[variant["grad_rule"]]
     p = O.Params(K=variant["K"], tau=6.0, calibration=cal, reconstruction=rec, surrogate=ste, grad_rule=rule)
     t0 = time.perf_counter()
     O.head_backward(q[b, h], k[b, h], v[b, h], do[b, h], p)   # runs the forward of every row too
@@ -233,7 +234,7 @@ def main():
     ap.add_argument("--calibration", choices=["minmax", "fwm"])
     ap.add_argument("--reconstruction", choices=["lerp", "nearest"])
     ap.add_argument("--surrogate", choices=["weight", "prob"])
-    ap.add_argument("--grad-rule", dest="grad_rule", choices=["full", "detach", "max_only", "min_only"])
+    ap.add_argument("--grad-rule", dest="grad_rule", choices=["full", "detach", "max_only", "min_only", "p1"])
     ap.add_argument("--cpu-slices", type=int, default=96,
                     help="oracle sample size for the CPU baseline, in (b, h) slices (capped at B*H)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -57,7 +57,10 @@ typedef enum kia_status {
 enum { KIA_CAL_MINMAX = 0, KIA_CAL_FWM = 1 };
 enum { KIA_REC_LERP = 0, KIA_REC_NEAREST = 1 };
 enum { KIA_STE_WEIGHT = 0, KIA_STE_PROB = 1 };  /* read only for Nearest */
-enum { KIA_GRAD_FULL = 0, KIA_GRAD_DETACH = 1, KIA_GRAD_MAX_ONLY = 2, KIA_GRAD_MIN_ONLY = 3 };
+enum { KIA_GRAD_FULL = 0, KIA_GRAD_DETACH = 1, KIA_GRAD_MAX_ONLY = 2, KIA_GRAD_MIN_ONLY = 3, KIA_GRAD_P1 = 4 };
+/* KIA_GRAD_P1 is the zero-sum projection of the detached gradient (App. B;
+ * section 5.1, "P1"): dS <- dS_detach - (mean of dS_detach over the row's
+ * causal keys).  Its forward is the detach forward, bit for bit. */
 
 /* Operator flags.  n_intervals is the method's K (grid of K+1 values); it is
  * named so it cannot be mistaken for the key tensor.  tau is the FWM window
@@ -94,12 +97,16 @@ typedef struct kia_stats_layout {
  * the score gradient dS (calibration terms included) as tiles in key-major
  * order (per (b, h): tile (qt, kt) at the same index as the score tiles), and
  * the per-row calibration terms the gradient rule routed to the argmax key
- * (cm) and the argmin key (cn), fp32 [B*H*T]. */
+ * (cm) and the argmin key (cn), fp32 [B*H*T].  Under KIA_GRAD_P1, cm holds
+ * the subtracted row mean and cn is 0, and two more sections hold the causal
+ * prefix sums of K ([B,H,T,d] fp32, prefix_k) and per-32-row chunk sums of K
+ * (chunk_k); both offsets are 0 under the other rules. */
 typedef struct kia_workspace_layout {
     size_t total_bytes;
     size_t probs;
     size_t dscores;
     size_t row_cm, row_cn;
+    size_t prefix_k, chunk_k;
 } kia_workspace_layout;
 
 /* Size queries.  Return 0 on invalid arguments (same checks as the calls). */

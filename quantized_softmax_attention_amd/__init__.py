@@ -20,7 +20,7 @@ from ._lib import KiaExt, KiaParams, KiaStatsLayout, KiaWorkspaceLayout
 CAL = {"minmax": 0, "fwm": 1}
 REC = {"lerp": 0, "nearest": 1}
 STE = {"weight": 0, "prob": 1}
-RULE = {"full": 0, "detach": 1, "max_only": 2, "min_only": 3}
+RULE = {"full": 0, "detach": 1, "max_only": 2, "min_only": 3, "p1": 4}
 
 
 class KiaError(RuntimeError):

@@ -26,7 +26,7 @@ class KiaStatsLayout(ctypes.Structure):
 
 class KiaWorkspaceLayout(ctypes.Structure):
     _fields_ = [("total_bytes", c_size_t), ("probs", c_size_t), ("dscores", c_size_t),
-                ("row_cm", c_size_t), ("row_cn", c_size_t)]
+                ("row_cm", c_size_t), ("row_cn", c_size_t), ("prefix_k", c_size_t), ("chunk_k", c_size_t)]
 
 
 class KiaExt(ctypes.Structure):

@@ -22,7 +22,7 @@ kia_status check_params(const kia_params* p) {
     if (p->calibration != KIA_CAL_MINMAX && p->calibration != KIA_CAL_FWM) return KIA_ERR_PARAM;
     if (p->reconstruction != KIA_REC_LERP && p->reconstruction != KIA_REC_NEAREST) return KIA_ERR_PARAM;
     if (p->surrogate != KIA_STE_WEIGHT && p->surrogate != KIA_STE_PROB) return KIA_ERR_PARAM;
-    if (p->grad_rule < KIA_GRAD_FULL || p->grad_rule > KIA_GRAD_MIN_ONLY) return KIA_ERR_PARAM;
+    if (p->grad_rule < KIA_GRAD_FULL || p->grad_rule > KIA_GRAD_P1) return KIA_ERR_PARAM;
     if (p->calibration == KIA_CAL_FWM && !(p->tau > 0.f && isfinite(p->tau))) return KIA_ERR_PARAM;
     return KIA_OK;
 }
@@ -67,7 +67,7 @@ void stats_layout(const kia_params* p, const Shape& s, kia_stats_layout* L) {
     L->tiles_per_head = s.tiles_per_head;
 }
 
-void workspace_layout(const Shape& s, kia_workspace_layout* L) {
+void workspace_layout(const kia_params* p, const Shape& s, kia_workspace_layout* L) {
     size_t off = 0;
     const size_t rows = (size_t)(s.BH * s.T);
     const size_t tiles = (size_t)s.BH * s.tiles_per_head * kia::kTileElems * 4;
@@ -75,6 +75,13 @@ void workspace_layout(const Shape& s, kia_workspace_layout* L) {
     L->dscores = off;  off = align_up(off + tiles);
     L->row_cm = off;   off = align_up(off + rows * 4);
     L->row_cn = off;   off = align_up(off + rows * 4);
+    if (p->grad_rule == KIA_GRAD_P1) {
+        L->prefix_k = off; off = align_up(off + rows * (size_t)s.d * 4);
+        L->chunk_k = off;  off = align_up(off + (size_t)s.BH * s.n_t * (size_t)s.d * 4);
+    } else {
+        L->prefix_k = 0;
+        L->chunk_k = 0;
+    }
     L->total_bytes = off;
 }
 
@@ -111,7 +118,7 @@ size_t kia_workspace_bytes(const kia_params* p, int B, int H, int T, int d) {
     Shape s;
     if (check_params(p) != KIA_OK || check_shape(B, H, T, d, &s) != KIA_OK) return 0;
     kia_workspace_layout L;
-    workspace_layout(s, &L);
+    workspace_layout(p, s, &L);
     return L.total_bytes;
 }
 
@@ -132,7 +139,7 @@ kia_status kia_workspace_layout_query(const kia_params* p, int B, int H, int T, 
     if (st != KIA_OK) return st;
     Shape s;
     if ((st = check_shape(B, H, T, d, &s)) != KIA_OK) return st;
-    workspace_layout(s, out);
+    workspace_layout(p, s, out);
     return KIA_OK;
 }
 
@@ -194,7 +201,7 @@ kia_status kia_backward_ext(const kia_params* p, int B, int H, int T, int d, con
     stats_layout(p, s, &L);
     if (stats_bytes < L.total_bytes) return KIA_ERR_BUFFER;
     kia_workspace_layout WL;
-    workspace_layout(s, &WL);
+    workspace_layout(p, s, &WL);
     if (ws_bytes < WL.total_bytes) return KIA_ERR_BUFFER;
     if (ext && ext->n_events < 0) return KIA_ERR_PARAM;
 
@@ -215,6 +222,10 @@ kia_status kia_backward_ext(const kia_params* p, int B, int H, int T, int d, con
     a.dscores = (float*)(wb + WL.dscores);
     a.row_cm = (float*)(wb + WL.row_cm);
     a.row_cn = (float*)(wb + WL.row_cn);
+    const bool p1 = p->grad_rule == KIA_GRAD_P1;
+    if (p1 && s.BH * s.tiles_per_head > INT32_MAX) return KIA_ERR_SHAPE;  // one-dimensional grid of the centring kernel
+    a.prefix_k = p1 ? (float*)(wb + WL.prefix_k) : nullptr;
+    a.chunk_k = p1 ? (float*)(wb + WL.chunk_k) : nullptr;
     a.BH = (int)s.BH; a.T = T; a.n_t = (int)s.n_t; a.K = p->n_intervals;
     a.tau = p->tau;
     a.scale = 1.f / sqrtf((float)d);
@@ -223,7 +234,9 @@ kia_status kia_backward_ext(const kia_params* p, int B, int H, int T, int d, con
     hipStream_t hs = (hipStream_t)stream;
     const kia::FwdConfig c = config_of(p, d, false);
     if ((st = record(ext, 0, hs)) != KIA_OK) return st;
+    if (p1 && kia::launch_key_prefix(d, a, hs) != hipSuccess) return KIA_ERR_HIP;
     if (kia::launch_backward_rows(c, a, hs) != hipSuccess) return KIA_ERR_HIP;
+    if (p1 && kia::launch_center_rows(a, hs) != hipSuccess) return KIA_ERR_HIP;
     if ((st = record(ext, 1, hs)) != KIA_OK) return st;
     if ((st = record(ext, 2, hs)) != KIA_OK) return st;
     if (kia::launch_backward_cols(d, a, hs) != hipSuccess) return KIA_ERR_HIP;
@@ -264,6 +277,6 @@ const char* kia_status_str(kia_status s) {
     return "unknown status";
 }
 
-int32_t kia_abi_version(void) { return 1; }
+int32_t kia_abi_version(void) { return 2; }
 
 }  // extern "C"

@@ -56,6 +56,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
     const int n_blk = (n_t + kBlockTiles - 1) / kBlockTiles;
     int bh, blk;
     map_block(blockIdx.x, a.BH, n_blk, true, bh, blk);
+    set_length_priority(blk + 1, n_blk);
     const int qt = blk * kBlockTiles + wave;
     const bool active = qt < n_t;
     const int kt_end = min(blk * kBlockTiles + kBlockTiles - 1, n_t - 1);
@@ -100,14 +101,18 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
     const float invW = 1.f / W;
     // a row with a single causal key has P = 1 whatever its score: zero gradient
     const float invWe = (qrow == 0) ? 0.f : ((REC == REC_NEAREST && PROB) ? 1.f / WL : invW);
+    // log2 of the row's 1/W, -inf for rows past the sequence end (their P and dS become 0)
+    const float lw = qvalid ? __log2f(invW) : -INFINITY;
+    const float nd = -dlt * invWe;               // G = (dP * invWe + nd) * g
+    const float gW = invWe * W, ndW = nd * W;    // the same with g / W folded into gw
 
-    // Row sums of the direct term (SA) and of dL/dw * Wd (SB, Wd = g * t).
+    // Row sums of the direct term (SA) and of dL/dw * Wd (SB = (c/h - 1) SBu + c SBf).
     // SA is summed per tile in fp32 (in key order, no contraction, so the
     // epilogue can reproduce a tile's partial bit for bit) and across tiles
     // with a compensated (hi, lo) pair.  SB / K enters the two routed terms
     // with opposite signs and cancels exactly, so an fp32 running sum
     // suffices for it.
-    float SA = 0.f, SB = 0.f;
+    float SA = 0.f, SBu = 0.f, SBf = 0.f;
     float SAhi = 0.f, SAlo = 0.f;  // compensated running sum of the per-tile SA
     f32x16 dq[NB];
 #pragma unroll
@@ -168,17 +173,31 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
                 for (int r = 0; r < 16; ++r) {
                     const int key = k0 + acc_row(r, hl);
                     const bool valid = DIAG ? key <= qrow : true;
-                    const Recon e = reconstruct<CAL, REC == REC_NEAREST>(rg, scur[r]);
-                    const bool keep = valid && e.inwin;
-                    const float wh = (REC == REC_LERP) ? e.wl : e.wn;
-                    pr[r] = (keep && qvalid) ? wh * invW : 0.f;
-                    // dL/dw times the grid value; the direct term and the h-derivative share it
-                    const float gtg = (dp[r] - dlt) * invWe * e.g;
-                    const float A = gtg * rg.coh;
-                    const float t = fmaf(rg.cohm1, e.u, e.f * fmaf(e.fi, rg.c, rg.c));
-                    ds[r] = keep ? A : 0.f;
+                    const float s = scur[r];
+                    const float u = (rg.m - s) * rg.invh;
+                    const bool keep = valid && ((CAL == CAL_MINMAX) ? true : (u <= rg.Kf));
+                    const float fi = fminf(floorf(u), rg.Kf - 1.f);
+                    const float f = u - fi;
+                    // G = dL/dw times the LERP segment's grid value g_i; the direct
+                    // term and the h-derivative share it
+                    float G, pw;
+                    if (REC == REC_LERP) {
+                        // gw = g_i / W in one exponential; P = gw (1 - f c)
+                        const float gw = fast_exp2(fmaf(-fi, rg.hl2, lw));
+                        pw = gw * fmaf(-f, rg.c, 1.f);
+                        G = fmaf(dp[r], gW, ndW) * gw;
+                    } else {
+                        const float g = fast_exp2(-fi * rg.hl2);
+                        pw = fast_exp2(fmaf(-floorf(u + 0.5f), rg.hl2, lw));
+                        G = fmaf(dp[r], invWe, nd) * g;
+                    }
+                    pr[r] = keep ? pw : 0.f;
+                    ds[r] = keep ? G * rg.coh : 0.f;
                     SA += ds[r];
-                    SB = keep ? fmaf(gtg, t, SB) : SB;
+                    // dL/dw * Wd with Wd / g = (c/h - 1) u + c f (i + 1)
+                    const float Gk = keep ? G : 0.f;
+                    SBu = fmaf(Gk, u, SBu);
+                    SBf = fmaf(Gk, fmaf(f, fi, f), SBf);
                 }
             };
             if (kt == qt) grads(std::true_type{});
@@ -227,7 +246,10 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
         lds_barrier();
     }
 
-    SB += __shfl_xor(SB, 32);
+    SBu += __shfl_xor(SBu, 32);
+    SBf += __shfl_xor(SBf, 32);
+    const float SB = rg.cohm1 * SBu + rg.c * SBf;
+    const bool p1 = a.rule == GRAD_P1;
     const bool use_max = !rg.degen && (a.rule == GRAD_FULL || a.rule == GRAD_MAX_ONLY);
     const bool use_min = !rg.degen && CAL == CAL_MINMAX && (a.rule == GRAD_FULL || a.rule == GRAD_MIN_ONLY);
     // causal key indices by construction; clamped so no stats value can address outside the row
@@ -266,6 +288,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
     if (CAL == CAL_MINMAX) sbk = (double)(SB / rg.Kf);
     const float cn = use_min ? (float)(-sbk) : 0.f;
 
+    // P1: the row mean of the detached gradient (0 for a single-key row)
+    const float mu = p1 ? (float)(sa_excl / (double)(qrow + 1)) : 0.f;
     if (qvalid) {
         float cm = 0.f;
         if (use_max) {
@@ -284,13 +308,15 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
                 const int c = 32 * b + 8 * p + 4 * hl;
                 const f32x4 xa = *(const f32x4*)(Kp + (size_t)ka * D + c);
                 const f32x4 xb = *(const f32x4*)(Kp + (size_t)kb * D + c);
+                f32x4 pk = {0.f, 0.f, 0.f, 0.f};
+                if (p1) pk = *(const f32x4*)(a.prefix_k + head + (size_t)qrow * D + c);
                 f32x4 y;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) y[j] = (dq[b][4 * p + j] + cm * xa[j] + cn * xb[j]) * a.scale;
+                for (int j = 0; j < 4; ++j) y[j] = (dq[b][4 * p + j] + cm * xa[j] + cn * xb[j] - mu * pk[j]) * a.scale;
                 *(f32x4*)(dqrow + c) = y;
             }
         if (hl == 0) {
-            a.row_cm[ri] = cm;
+            a.row_cm[ri] = p1 ? mu : cm;
             a.row_cn[ri] = cn;
             // argmax != argmin whenever C_n is routed (non-degenerate rows)
             if (cn != 0.f) {
@@ -317,6 +343,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_cols
     const int n_blk = (n_t + kBlockTiles - 1) / kBlockTiles;
     int bh, blk;
     map_block(blockIdx.x, a.BH, n_blk, false, bh, blk);
+    set_length_priority(n_blk - blk, n_blk);
     const int kt = blk * kBlockTiles + wave;
     const bool active = kt < n_t;
     const int qt_begin = blk * kBlockTiles;
@@ -441,11 +468,8 @@ __global__ __launch_bounds__(256) void kia_tiles_to_dense_kernel(int T, int n_t,
                                                                  int key_major, float* dense) {
     const int bh = blockIdx.y;
     const int ti = blockIdx.x;
-    // recover (qt, kt) from the triangular index qt*(qt+1)/2 + kt
-    int qt = (int)((sqrtf(8.f * ti + 1.f) - 1.f) * 0.5f);
-    while ((int64_t)qt * (qt + 1) / 2 > ti) --qt;
-    while ((int64_t)(qt + 1) * (qt + 2) / 2 <= ti) ++qt;
-    const int kt = ti - (int)tile_index(qt, 0);
+    int qt, kt;
+    tile_coords(ti, qt, kt);
     const int64_t tiles_per_head = (int64_t)n_t * (n_t + 1) / 2;
     const float* tp = tiles + ((size_t)bh * tiles_per_head + ti) * kTileElems;
     for (int e = threadIdx.x; e < kTileElems; e += blockDim.x) {

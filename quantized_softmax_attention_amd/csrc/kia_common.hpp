@@ -27,7 +27,7 @@ constexpr int kWave = 64;
 
 enum { CAL_MINMAX = 0, CAL_FWM = 1 };
 enum { REC_LERP = 0, REC_NEAREST = 1 };
-enum { GRAD_FULL = 0, GRAD_DETACH = 1, GRAD_MAX_ONLY = 2, GRAD_MIN_ONLY = 3 };
+enum { GRAD_FULL = 0, GRAD_DETACH = 1, GRAD_MAX_ONLY = 2, GRAD_MIN_ONLY = 3, GRAD_P1 = 4 };
 
 // Spans below this take the degenerate branch (App. A: branches for spans
 // above or below 1e-12).
@@ -271,6 +271,29 @@ __device__ __forceinline__ void pin_interleave() {
     for (int s = 0; s < NS; ++s) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
         __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);  // VALU
+    }
+}
+
+// (qt, kt) of the triangular tile index ti = qt*(qt+1)/2 + kt.
+__device__ __forceinline__ void tile_coords(int ti, int& qt, int& kt) {
+    qt = (int)((sqrtf(8.f * ti + 1.f) - 1.f) * 0.5f);
+    while ((int64_t)qt * (qt + 1) / 2 > ti) --qt;
+    while ((int64_t)(qt + 1) * (qt + 2) / 2 <= ti) ++qt;
+    kt = ti - (int)((int64_t)qt * (qt + 1) / 2);
+}
+
+// Wave priority by block length.  Blocks of a causal slice differ in length
+// by up to n_blk x, and two workgroups share each CU; raising the issue
+// priority of the longer block's waves (0..3 in proportion to its length)
+// lets the launch's critical path run ahead while shorter blocks fill the
+// remaining issue slots.  len is the block's tile count, max_len the longest.
+__device__ __forceinline__ void set_length_priority(int len, int max_len) {
+    const int prio = max_len > 0 ? min(3, (4 * len - 1) / max_len) : 0;
+    switch (prio) {
+        case 3: __builtin_amdgcn_s_setprio(3); break;
+        case 2: __builtin_amdgcn_s_setprio(2); break;
+        case 1: __builtin_amdgcn_s_setprio(1); break;
+        default: break;
     }
 }
 

@@ -44,6 +44,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
     const int n_blk = (n_t + kBlockTiles - 1) / kBlockTiles;
     int bh, blk;
     map_block(blockIdx.x, a.BH, n_blk, true, bh, blk);
+    set_length_priority(blk + 1, n_blk);
     const int qt = blk * kBlockTiles + wave;                   // this wave's query tile
     const bool active = qt < n_t;
     const int kt_end = min(blk * kBlockTiles + kBlockTiles - 1, n_t - 1);  // last key tile of the block

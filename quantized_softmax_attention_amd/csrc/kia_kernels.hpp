@@ -43,8 +43,10 @@ struct BwdArgs {
     float* dv;
     float* probs;        // key-major P tiles
     float* dscores;      // key-major dS tiles (calibration terms folded in)
-    float* row_cm;
+    float* row_cm;       // P1: the subtracted row mean
     float* row_cn;
+    float* prefix_k;     // P1 only: sum_{j <= t} K_j per row, [BH, T, d]
+    float* chunk_k;      // P1 only: per-32-row chunk sums of K, [BH, n_t, d]
     int BH, T, n_t, K;
     float tau, scale;
     int rule;
@@ -58,6 +60,8 @@ struct FwdConfig {
 hipError_t launch_forward(const FwdConfig& c, const FwdArgs& a, hipStream_t s);
 hipError_t launch_backward_rows(const FwdConfig& c, const BwdArgs& a, hipStream_t s);
 hipError_t launch_backward_cols(int d, const BwdArgs& a, hipStream_t s);
+hipError_t launch_key_prefix(int d, const BwdArgs& a, hipStream_t s);
+hipError_t launch_center_rows(const BwdArgs& a, hipStream_t s);
 hipError_t launch_tiles_to_dense(int BH, int T, const float* tiles, int key_major, float* dense,
                                  hipStream_t s);
 

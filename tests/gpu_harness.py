@@ -31,7 +31,8 @@ def to_oracle_params(p):
     cal = {"minmax": O.MINMAX, "fwm": O.FWM}[p.calibration]
     rec = {"lerp": O.LERP, "nearest": O.NEAREST}[p.reconstruction]
     ste = {"weight": O.WEIGHT_STE, "prob": O.PROB_STE}[p.surrogate]
-    rule = {"full": O.FULL, "detach": O.DETACH, "max_only": O.MAX_ONLY, "min_only": O.MIN_ONLY}[p.grad_rule]
+    rule = {"full": O.FULL, "detach": O.DETACH, "max_only": O.MAX_ONLY, "min_only": O.MIN_ONLY,
+            "p1": O.P1}[p.grad_rule]
     return O.Params(K=p.K, tau=p.tau, calibration=cal, reconstruction=rec, surrogate=ste, grad_rule=rule)
 
 

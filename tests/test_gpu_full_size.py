@@ -65,12 +65,12 @@ def full_check(name, params, heads, rows=None, tail=None, zero_sum=None):
             err, kept = sc.compare(nm)
             worst[nm] = max(worst.get(nm, 0.0), err)
             assert err <= TOL, f"{nm} rel err {err:.3e} in slice {(b, h)} ({kept} compared)"
-        if params.grad_rule == "full":
+        if params.grad_rule in ("full", "p1"):
             bad = sc.zero_sum_violations(q, k, v, do, b, h)
             assert not bad, f"zero-sum violated in slice {(b, h)}: {bad[:3]}"
         ties += int(sc.amb_bwd.sum())
         excluded += sc.n_amb_pairs
-    if zero_sum if zero_sum is not None else params.grad_rule == "full":
+    if zero_sum if zero_sum is not None else params.grad_rule in ("full", "p1"):
         nbad, nrows, detail = zero_sum_all_rows(g)
         assert nbad == 0, f"{nbad} of {nrows} rows violate the zero row sum: (b,h,t), sum, L1, a, b, cm, cn = {detail}"
         print(f"  zero row sum holds on all {nrows} rows", flush=True)
@@ -89,6 +89,13 @@ def test_c2_full_size(K, rule):
     i = [4, 16, 32].index(K) * 4 + ["full", "detach", "max_only", "min_only"].index(rule)
     full_check("c2", P(K=K, calibration="minmax", reconstruction="lerp", grad_rule=rule),
                _heads(i, WORKLOADS["c2"]))
+
+
+@pytest.mark.parametrize("K", [4, 32])
+def test_c2_full_size_p1(K):
+    """P1 (zero-sum projection of the detached gradient) at full size."""
+    full_check("c2", P(K=K, calibration="minmax", reconstruction="lerp", grad_rule="p1"),
+               _heads(13 + K, WORKLOADS["c2"]))
 
 
 @pytest.mark.parametrize("cal", ["minmax", "fwm"])
@@ -148,10 +155,10 @@ def _fwd(name, params):
 
 def test_forward_identical_across_gradient_rules():
     """The forward never reads the gradient rule: O, scores and row statistics
-    are bitwise equal under all four rules."""
+    are bitwise equal under all five rules (P1's forward is detach's)."""
     print("[case] c2 forward identity across rules", flush=True)
     ref_o, ref_st = _fwd("c2", P(K=32, grad_rule="full"))
-    for rule in ("detach", "max_only", "min_only"):
+    for rule in ("detach", "max_only", "min_only", "p1"):
         o, st = _fwd("c2", P(K=32, grad_rule=rule))
         assert np.array_equal(o.view(np.uint32), ref_o.view(np.uint32)), rule
         assert np.array_equal(st, ref_st), rule

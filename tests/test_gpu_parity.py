@@ -38,7 +38,7 @@ def check(w: Workload, params, heads=None, max_amb_frac=0.02, verbose=True):
             err, kept = sc.compare(name)
             worst[name] = max(worst.get(name, 0.0), err)
             assert err <= TOL, f"{name} rel err {err:.3e} in slice {(b, h)} ({kept} rows compared)"
-        if params.grad_rule == "full":
+        if params.grad_rule in ("full", "p1"):
             bad = sc.zero_sum_violations(q, k, v, do, b, h)
             assert not bad, f"zero-sum violated in slice {(b, h)}: {bad[:3]}"
         n_amb += sc.n_amb_pairs
@@ -55,7 +55,7 @@ SMALL128 = Workload("small_ragged_d128", 1, 2, 75, 128, "head_temp", lo=0.5, hi=
 COMBOS = [("minmax", "lerp", "weight"), ("fwm", "lerp", "weight"),
           ("minmax", "nearest", "weight"), ("minmax", "nearest", "prob"),
           ("fwm", "nearest", "weight"), ("fwm", "nearest", "prob")]
-RULES = ["full", "detach", "max_only", "min_only"]
+RULES = ["full", "detach", "max_only", "min_only", "p1"]
 
 
 @pytest.mark.parametrize("cal,rec,ste", COMBOS)

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), f"libkia.so does not export {name}"
         assert name in mod.SIGNATURES, f"binding has no signature for {name}"
     assert set(mod.SIGNATURES) == set(names)
-    assert lib.kia_abi_version() == 1
+    assert lib.kia_abi_version() == 2
 
 
 def _params(mod, K=4, tau=6.0, cal=0, rec=0, ste=0, rule=0):
@@ -72,6 +72,13 @@ def test_size_queries():
     W = mod.KiaWorkspaceLayout()
     assert lib.kia_workspace_layout_query(ctypes.byref(p), B, H, T, d, ctypes.byref(W)) == 0
     assert W.total_bytes == wb and W.dscores >= W.probs + tiles
+    assert W.prefix_k == 0 and W.chunk_k == 0
+    # P1 adds the causal prefix sums of K and their chunk sums
+    p1 = _params(mod, rule=4)
+    W1 = mod.KiaWorkspaceLayout()
+    assert lib.kia_workspace_layout_query(ctypes.byref(p1), B, H, T, d, ctypes.byref(W1)) == 0
+    assert W1.prefix_k >= W1.row_cn + B * H * T * 4 and W1.chunk_k >= W1.prefix_k + B * H * T * d * 4
+    assert W1.total_bytes >= W1.chunk_k + B * H * n_t * d * 4
     # invalid arguments size to zero
     assert lib.kia_stats_bytes(ctypes.byref(p), B, H, T, 96) == 0
     assert lib.kia_stats_bytes(ctypes.byref(_params(mod, K=0)), B, H, T, d) == 0
@@ -94,7 +101,7 @@ def _bwd(lib, p, ptrs=None, nbytes=1 << 40, wbytes=1 << 40, T=8, d=64):
 
 
 @pytest.mark.parametrize("field,value", [("n_intervals", 0), ("n_intervals", 65537), ("calibration", 2),
-                                         ("reconstruction", -1), ("surrogate", 3), ("grad_rule", 4)])
+                                         ("reconstruction", -1), ("surrogate", 3), ("grad_rule", 5)])
 def test_bad_params_rejected(field, value):
     lib, mod = _lib()
     p = _params(mod)
