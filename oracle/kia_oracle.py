@@ -44,6 +44,16 @@ Readings where the pages leave a step open (each is listed in the design doc):
   R7  Scores are Q.K / sqrt(d); key t is causal for query t.
   R8  P1 (zero-sum projection of the detached gradient, App. B; section 5.1):
       dS <- dS_detach - mean over the row's causal keys.
+  R11 The untruncated fixed-step operator (App. D.4, "tail policy"): FWM's
+      step h = tau/K anchored at the max, with the grid continued below
+      max - tau instead of a zero tail: LERP segment i = floor(u) and Nearest
+      point r = floor(u + 1/2) without an upper bound, so every causal key
+      keeps a nonzero weight.  Only the max carries a calibration term (h is
+      fixed).
+  R12 The exact-softmax reference on the same path (App. D.5 compares the
+      operator against softmax): w = exp(s - m); the calibration and
+      surrogate flags are ignored; its calibration term through m vanishes
+      up to rounding, so every rule gives the softmax gradient P (dP - delta).
 
 Parity: every function below is pinned by the CPU tests (closed forms,
 brute force, finite differences, an autograd re-expression, the softmax
@@ -55,8 +65,8 @@ from dataclasses import dataclass
 
 import numpy as np
 
-MINMAX, FWM = 0, 1
-LERP, NEAREST = 0, 1
+MINMAX, FWM, FWM_UNTRUNC = 0, 1, 2
+LERP, NEAREST, EXACT = 0, 1, 2
 WEIGHT_STE, PROB_STE = 0, 1
 FULL, DETACH, MAX_ONLY, MIN_ONLY, P1 = 0, 1, 2, 3, 4
 
@@ -76,7 +86,7 @@ class Params:
         return self.grad_rule in (FULL, MAX_ONLY)
 
     def carries_min(self) -> bool:
-        return self.grad_rule in (FULL, MIN_ONLY) and self.calibration == MINMAX
+        return self.grad_rule in (FULL, MIN_ONLY) and self.calibration == MINMAX and self.reconstruction != EXACT
 
 
 # ---------------------------------------------------------------------------
@@ -100,11 +110,13 @@ class Calibration:
 
 
 def calibrate(s: np.ndarray, p: Params) -> Calibration:
-    """Row calibration: MinMax h = span/K, FWM h = tau/K (section 3; App. A)."""
+    """Row calibration: MinMax h = span/K, FWM h = tau/K (section 3; App. A).
+    The untruncated fixed step (App. D.4) uses FWM's h = tau/K; the exact
+    softmax reference uses only the max (its h is unused)."""
     a = int(np.argmax(s))   # numpy returns the first maximal index
     b = int(np.argmin(s))
     m, n = float(s[a]), float(s[b])
-    if p.calibration == MINMAX:
+    if p.calibration == MINMAX and p.reconstruction != EXACT:
         span = m - n
         if span < EPS_SPAN:
             return Calibration(m, a, n, b, 0.0, True)
@@ -121,12 +133,14 @@ def grid(h: float, K: int) -> np.ndarray:
 class Recon:
     """Per-key reconstruction state of one row."""
     u: np.ndarray      # (m - s)/h, distance below the max in grid steps
-    uc: np.ndarray     # u clamped to K (rounding guard, not differentiated)
-    mask: np.ndarray   # 1 in the window (always 1 for MinMax)
+    uc: np.ndarray     # u clamped to K (rounding guard, not differentiated; unclamped untruncated)
+    mask: np.ndarray   # 1 in the window (always 1 for MinMax and the untruncated step)
     i: np.ndarray      # LERP segment
     f: np.ndarray      # position inside the segment
     r: np.ndarray      # Nearest grid point
-    g: np.ndarray      # the grid
+    g: np.ndarray      # the grid values exp(-j h), j = 0..K
+    gi: np.ndarray     # exp(-i h) at each key's segment start
+    gi1: np.ndarray    # exp(-(i+1) h) at its end
     wL: np.ndarray     # LERP weights
     wN: np.ndarray     # Nearest weights
 
@@ -144,14 +158,21 @@ def reconstruct(s: np.ndarray, m: float, h: float, p: Params, clamp: bool = True
         mask = (u <= K).astype(np.float64)                     # R5
     else:
         mask = np.ones_like(u)
-    uc = np.minimum(u, float(K)) if clamp else u.copy()
     g = grid(h, K)
-    i = np.clip(np.floor(uc), 0, K - 1).astype(np.int64)      # R2
+    if p.calibration == FWM_UNTRUNC:
+        # the grid continues below max - tau (App. D.4): no clamp, no tail mask (R11)
+        uc = u.copy()
+        i = np.maximum(np.floor(uc), 0).astype(np.int64)
+        r = np.maximum(np.floor(uc + 0.5), 0).astype(np.int64)
+    else:
+        uc = np.minimum(u, float(K)) if clamp else u.copy()
+        i = np.clip(np.floor(uc), 0, K - 1).astype(np.int64)      # R2
+        r = np.clip(np.floor(uc + 0.5), 0, K).astype(np.int64)    # R1
     f = uc - i
-    wL = mask * ((1.0 - f) * g[i] + f * g[i + 1])               # linear interpolation
-    r = np.clip(np.floor(uc + 0.5), 0, K).astype(np.int64)    # R1
-    wN = mask * g[r]
-    return Recon(u, uc, mask, i, f, r, g, wL, wN)
+    gi, gi1 = np.exp(-h * i), np.exp(-h * (i + 1))
+    wL = mask * ((1.0 - f) * gi + f * gi1)                      # linear interpolation
+    wN = mask * np.exp(-h * r)
+    return Recon(u, uc, mask, i, f, r, g, gi, gi1, wL, wN)
 
 
 @dataclass
@@ -168,6 +189,10 @@ class RowForward:
 
 def row_forward(s: np.ndarray, p: Params) -> RowForward:
     cal = calibrate(s, p)
+    if p.reconstruction == EXACT:                               # R12: exact softmax
+        w = np.exp(s - cal.m)
+        W = float(w.sum())
+        return RowForward(s, cal, None, w, W, w / W, w, W)
     if cal.degenerate:                                          # R4
         w = np.ones_like(s)
         W = float(w.sum())
@@ -193,6 +218,17 @@ class RowBackward:
 def row_backward(fw: RowForward, dP: np.ndarray, p: Params) -> RowBackward:
     """Score gradient of one row given dP_j = dO_t . V_j (App. B)."""
     cal, rec = fw.cal, fw.rec
+    if p.reconstruction == EXACT:                               # R12
+        delta = float(np.dot(fw.P, dP))
+        gt = (dP - delta) / fw.W
+        dS_direct = gt * fw.w                                   # d exp(s - m) / ds
+        Cm = -float(np.sum(gt * fw.w))                          # through the shift m (0 up to rounding)
+        dS = dS_direct.copy()
+        if p.grad_rule == P1:
+            dS = dS - dS.mean()
+        elif p.carries_max():
+            dS[cal.a] += Cm
+        return RowBackward(dS, dS_direct, gt, Cm, 0.0, delta, fw.W)
     if cal.degenerate:                                          # R4: softmax limit
         delta = float(np.dot(fw.P, dP))
         dS = fw.P * (dP - delta)
@@ -208,9 +244,9 @@ def row_backward(fw: RowForward, dP: np.ndarray, p: Params) -> RowBackward:
     gt = (dP - delta) / We                                      # dL/dw_j
 
     # LERP derivatives (the surrogate for Nearest), zero outside the window
-    g, i, f, h, K = rec.g, rec.i, rec.f, cal.h, p.K
-    dw_du = rec.mask * (g[i + 1] - g[i])
-    dw_dh = rec.mask * ((1.0 - f) * (-i * g[i]) + f * (-(i + 1) * g[i + 1]))
+    gi, gi1, i, f, h, K = rec.gi, rec.gi1, rec.i, rec.f, cal.h, p.K
+    dw_du = rec.mask * (gi1 - gi)
+    dw_dh = rec.mask * ((1.0 - f) * (-i * gi) + f * (-(i + 1) * gi1))
     du_ds = -1.0 / h
     du_dm = 1.0 / h
     du_dh = -rec.uc / h

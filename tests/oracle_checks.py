@@ -24,6 +24,10 @@ def surrogate_objective(mod, s, s0, dP, p):
     live_min = p.grad_rule in (mod.FULL, mod.MIN_ONLY)
     m = s.max() if live_max else cal0.m
     n = s.min() if live_min else cal0.n
+    if p.reconstruction == mod.EXACT:
+        w = np.exp(s - m)
+        rec = mod.reconstruct(s, m, 1.0, mod.Params(K=1))       # placeholder decisions (none)
+        return float((w / w.sum()) @ dP), rec
     h = (m - n) / p.K if p.calibration == mod.MINMAX else p.tau / p.K
     rec = mod.reconstruct(s, m, h, p, clamp=False)
     rec0 = mod.reconstruct(s0, cal0.m, cal0.h, p, clamp=False)
@@ -105,6 +109,10 @@ def torch_reexpression(mod, p, Q, Kt, V, dO):
             m = m.detach()
         if p.grad_rule in (mod.DETACH, mod.MAX_ONLY, mod.P1):
             n = n.detach()
+        if p.reconstruction == mod.EXACT:
+            w = torch.exp(s - m)
+            outs.append((w / w.sum()) @ v[: t + 1])
+            continue
         if p.calibration == mod.MINMAX:
             if float((m - n).detach()) < mod.EPS_SPAN:
                 w = torch.ones_like(s)
@@ -115,11 +123,16 @@ def torch_reexpression(mod, p, Q, Kt, V, dO):
             h = torch.tensor(p.tau / p.K, dtype=torch.float64)
         u = (m - s) / h
         mask = (u <= p.K).double().detach() if p.calibration == mod.FWM else torch.ones_like(u)
-        uc = u - (u - p.K).clamp(min=0).detach()        # value min(u, K), derivative 1
-        i = torch.floor(uc).clamp(0, p.K - 1).detach()
+        if p.calibration == mod.FWM_UNTRUNC:             # the grid continues below max - tau
+            uc = u
+            i = torch.floor(uc).clamp(min=0).detach()
+            r = torch.floor(uc + 0.5).clamp(min=0).detach()
+        else:
+            uc = u - (u - p.K).clamp(min=0).detach()    # value min(u, K), derivative 1
+            i = torch.floor(uc).clamp(0, p.K - 1).detach()
+            r = torch.floor(uc + 0.5).clamp(0, p.K).detach()
         f = uc - i
         wL = mask * ((1 - f) * torch.exp(-i * h) + f * torch.exp(-(i + 1) * h))
-        r = torch.floor(uc + 0.5).clamp(0, p.K).detach()
         wN = mask * torch.exp(-r * h)
         if p.reconstruction == mod.LERP:
             P = wL / wL.sum()

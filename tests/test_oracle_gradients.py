@@ -16,8 +16,8 @@ RULES = [O.FULL, O.DETACH, O.MAX_ONLY, O.MIN_ONLY]
 SURR = [(O.LERP, O.WEIGHT_STE), (O.NEAREST, O.WEIGHT_STE), (O.NEAREST, O.PROB_STE)]
 
 
-@pytest.mark.parametrize("cal", [O.MINMAX, O.FWM])
-@pytest.mark.parametrize("rec,ste", SURR)
+@pytest.mark.parametrize("cal", [O.MINMAX, O.FWM, O.FWM_UNTRUNC])
+@pytest.mark.parametrize("rec,ste", SURR + [(O.EXACT, O.WEIGHT_STE)])
 @pytest.mark.parametrize("rule", RULES)
 @pytest.mark.parametrize("K", [1, 4, 16])
 def test_score_level_finite_differences(cal, rec, ste, rule, K):
@@ -28,7 +28,7 @@ def test_score_level_finite_differences(cal, rec, ste, rule, K):
                              surrogate=ste, grad_rule=rule), s, dP)
 
 
-@pytest.mark.parametrize("cal", [O.MINMAX, O.FWM])
+@pytest.mark.parametrize("cal", [O.MINMAX, O.FWM, O.FWM_UNTRUNC])
 def test_qkv_finite_differences_lerp_full(cal):
     rng = np.random.default_rng(21)
     T, d = 6, 4
@@ -36,8 +36,8 @@ def test_qkv_finite_differences_lerp_full(cal):
     check_qkv_fd(O, Params(K=4, tau=3.0, calibration=cal), Q, Kt, V, dO)
 
 
-@pytest.mark.parametrize("cal", [O.MINMAX, O.FWM])
-@pytest.mark.parametrize("rec,ste", SURR)
+@pytest.mark.parametrize("cal", [O.MINMAX, O.FWM, O.FWM_UNTRUNC])
+@pytest.mark.parametrize("rec,ste", SURR + [(O.EXACT, O.WEIGHT_STE)])
 @pytest.mark.parametrize("rule", RULES + [O.P1])
 def test_autograd_reexpression(cal, rec, ste, rule):
     rng = np.random.default_rng(31)
@@ -87,7 +87,7 @@ def _head_inputs(seed=8, T=6, d=4):
 MUTANTS = [
     # (description, old, new, check)
     ("drop the i+1 grid-value term of dw/dh",
-     "f * (-(i + 1) * g[i + 1])", "f * (-i * g[i + 1])",
+     "f * (-(i + 1) * gi1)", "f * (-i * gi1)",
      lambda m: check_score_fd(m, m.Params(K=4), *_row_inputs())),
     ("route the min term with the max term's dh",
      "Cn = float(np.sum(gt * dw_dh_total * dh_dn))", "Cn = float(np.sum(gt * dw_dh_total * dh_dm))",
@@ -100,7 +100,8 @@ MUTANTS = [
      lambda m: check_score_fd(m, m.Params(K=4, reconstruction=m.NEAREST, surrogate=m.PROB_STE),
                               *_row_inputs())),
     ("detach that keeps the max term",
-     "if p.carries_max():", "if True:",
+     "        if p.carries_max():\n            dS[cal.a] += Cm\n        if p.carries_min():",
+     "        if True:\n            dS[cal.a] += Cm\n        if p.carries_min():",
      lambda m: check_score_fd(m, m.Params(K=4, grad_rule=m.DETACH), *_row_inputs())),
     ("dK built from dO instead of Q (transposed operand)",
      "dK[: t + 1] += np.outer(bw.dS, Q64[t]) * scale", "dK[: t + 1] += np.outer(bw.dS, dO64[t]) * scale",
@@ -112,6 +113,15 @@ MUTANTS = [
      "return (keys.astype(np.float64) @ q_t.astype(np.float64)) / np.sqrt(d)",
      "return (keys.astype(np.float64) @ q_t.astype(np.float64))",
      lambda m: check_autograd(m, m.Params(K=4), *_head_inputs(T=12, d=6))),
+    ("untruncated step keeps FWM's zero tail",
+     "        mask = np.ones_like(u)\n    g = grid(h, K)", "        mask = (u <= K).astype(np.float64)\n    g = grid(h, K)",
+     lambda m: check_autograd(m, m.Params(K=2, tau=1.0, calibration=m.FWM_UNTRUNC), *_head_inputs(T=12, d=6))),
+    ("untruncated step clamps its segment at K - 1",
+     "i = np.maximum(np.floor(uc), 0).astype(np.int64)", "i = np.clip(np.floor(uc), 0, K - 1).astype(np.int64)",
+     lambda m: check_autograd(m, m.Params(K=2, tau=1.0, calibration=m.FWM_UNTRUNC), *_head_inputs(T=12, d=6))),
+    ("exact softmax gradient taken at the unnormalised weights",
+     "gt = (dP - delta) / fw.W\n        dS_direct = gt * fw.w", "gt = (dP - delta)\n        dS_direct = gt * fw.w",
+     lambda m: check_autograd(m, m.Params(K=4, reconstruction=m.EXACT), *_head_inputs(T=12, d=6))),
     ("Nearest truncates instead of rounding (forward checked by autograd forward value)",
      "r = np.clip(np.floor(uc + 0.5), 0, K)", "r = np.clip(np.floor(uc), 0, K)",
      lambda m: check_autograd(m, m.Params(K=4, reconstruction=m.NEAREST), *_head_inputs(T=12, d=6))),

@@ -329,3 +329,71 @@ def test_weighted_orthogonality_at_evaluation_point(rec, ste):
     if rec == O.NEAREST:   # the other placement's weights are not orthogonal in general
         wo = fw.w if ste == O.PROB_STE else fw.wL
         assert abs(np.dot(bw.gt, wo)) > 1e-8 * np.abs(bw.gt).sum()
+
+
+# --------------------------------------------------------------------------
+# untruncated fixed step (App. D.4) and the exact-softmax reference (App. D.5)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rec,ste", ALL_SURROGATES)
+@pytest.mark.parametrize("rule", [O.FULL, O.DETACH])
+def test_untruncated_equals_fwm_inside_the_window(rec, ste, rule):
+    """With every score within tau of the max the tail is empty, so the
+    untruncated step and FWM coincide, forward and backward."""
+    rng = np.random.default_rng(41)
+    s = rng.uniform(-5.5, 0.0, 30)
+    s[3] = 0.0
+    dP = rng.standard_normal(30)
+    kw = dict(K=8, tau=6.0, reconstruction=rec, surrogate=ste, grad_rule=rule)
+    fa, fb = O.row_forward(s, Params(calibration=O.FWM, **kw)), O.row_forward(s, Params(calibration=O.FWM_UNTRUNC, **kw))
+    np.testing.assert_array_equal(fa.w, fb.w)
+    ba = O.row_backward(fa, dP, Params(calibration=O.FWM, **kw))
+    bb = O.row_backward(fb, dP, Params(calibration=O.FWM_UNTRUNC, **kw))
+    np.testing.assert_allclose(bb.dS, ba.dS, rtol=0, atol=1e-15)
+
+
+def test_untruncated_tail_key_closed_form():
+    """A key 2.5 steps past the window edge lies on segment K+2 at f = 1/2: its
+    LERP weight is the mean of exp(-(K+2) h) and exp(-(K+3) h) (nonzero, where
+    FWM gives 0); Nearest rounds it up to exp(-(K+3) h)."""
+    K, tau = 4, 6.0
+    h = tau / K
+    s = np.array([0.0, -0.3, -(K + 2.5) * h])
+    pl = Params(K=K, tau=tau, calibration=O.FWM_UNTRUNC)
+    w = O.row_forward(s, pl).w
+    assert w[2] == pytest.approx(0.5 * (np.exp(-(K + 2) * h) + np.exp(-(K + 3) * h)), rel=1e-12)
+    assert O.row_forward(s, Params(K=K, tau=tau, calibration=O.FWM)).w[2] == 0.0
+    wn = O.row_forward(s, Params(K=K, tau=tau, calibration=O.FWM_UNTRUNC, reconstruction=O.NEAREST)).w
+    assert wn[2] == pytest.approx(np.exp(-(K + 3) * h), rel=1e-12)
+
+
+def test_untruncated_converges_to_softmax():
+    """With tau fixed and K growing the step h = tau/K shrinks and no key is
+    dropped, so P tends to softmax(s) with the LERP error O(h^2): each doubling
+    of K cuts the error by about 4."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(43)
+    s = rng.standard_normal(40) * 4.0
+    ref = softmax(s)
+    errs = [np.abs(O.row_forward(s, Params(K=K, tau=3.0, calibration=O.FWM_UNTRUNC)).P - ref).max()
+            for K in (8, 16, 32, 64)]
+    rates = [errs[i] / errs[i + 1] for i in range(3)]
+    assert np.mean(rates) == pytest.approx(4.0, rel=0.2), rates
+    assert errs[-1] < 1e-3
+
+
+@pytest.mark.parametrize("rule", [O.FULL, O.DETACH, O.MAX_ONLY, O.MIN_ONLY, O.P1])
+def test_exact_reference_is_softmax(rule):
+    """The exact reference is softmax attention: P = softmax(s) (a library
+    routine) and, under every rule, dS = P (dP - P.dP), the softmax
+    Jacobian, which already sums to zero."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(44)
+    s = rng.standard_normal(25) * 3.0
+    dP = rng.standard_normal(25)
+    p = Params(K=4, reconstruction=O.EXACT, grad_rule=rule)
+    fw = O.row_forward(s, p)
+    P = softmax(s)
+    np.testing.assert_allclose(fw.P, P, rtol=1e-13, atol=0)
+    bw = O.row_backward(fw, dP, p)
+    np.testing.assert_allclose(bw.dS, P * (dP - P @ dP), rtol=0, atol=1e-14)
