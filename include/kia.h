@@ -48,14 +48,23 @@ typedef enum kia_status {
     KIA_OK = 0,
     KIA_ERR_NULL = 1,      /* a required pointer is NULL */
     KIA_ERR_SHAPE = 2,     /* B, H, T < 1, d not in {64, 128}, or sizes overflow */
-    KIA_ERR_PARAM = 3,     /* flag out of range, n_intervals < 1, tau <= 0 under FWM */
+    KIA_ERR_PARAM = 3,     /* flag out of range, n_intervals < 1, tau <= 0 under FWM / FWM_UNTRUNC */
     KIA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned */
     KIA_ERR_BUFFER = 5,    /* stats or workspace smaller than the size query returns */
     KIA_ERR_HIP = 6        /* a kernel launch failed */
 } kia_status;
 
-enum { KIA_CAL_MINMAX = 0, KIA_CAL_FWM = 1 };
-enum { KIA_REC_LERP = 0, KIA_REC_NEAREST = 1 };
+enum { KIA_CAL_MINMAX = 0, KIA_CAL_FWM = 1, KIA_CAL_FWM_UNTRUNC = 2 };
+enum { KIA_REC_LERP = 0, KIA_REC_NEAREST = 1, KIA_REC_EXACT = 2 };
+/* KIA_CAL_FWM_UNTRUNC is the untruncated fixed-step operator of the paper's
+ * tail-policy comparison (App. D.4): FWM's step h = tau/K anchored at the row
+ * max, with the grid continued below max - tau instead of a zero tail (the
+ * LERP segment and the Nearest point are unbounded; only the max carries a
+ * calibration term).  KIA_REC_EXACT is the exact-softmax reference on the
+ * same path (App. D.5 compares against softmax): w = exp(s - max), with the
+ * calibration, tau and surrogate flags ignored; its calibration term through
+ * the max vanishes up to rounding, so every rule yields the softmax
+ * gradient. */
 enum { KIA_STE_WEIGHT = 0, KIA_STE_PROB = 1 };  /* read only for Nearest */
 enum { KIA_GRAD_FULL = 0, KIA_GRAD_DETACH = 1, KIA_GRAD_MAX_ONLY = 2, KIA_GRAD_MIN_ONLY = 3, KIA_GRAD_P1 = 4 };
 /* KIA_GRAD_P1 is the zero-sum projection of the detached gradient (App. B;
@@ -70,7 +79,7 @@ enum { KIA_GRAD_FULL = 0, KIA_GRAD_DETACH = 1, KIA_GRAD_MAX_ONLY = 2, KIA_GRAD_M
  * min plays no role: MIN_ONLY behaves as DETACH and MAX_ONLY as FULL. */
 typedef struct kia_params {
     int32_t n_intervals;     /* 1 .. 65536 */
-    float tau;               /* > 0 and finite under FWM */
+    float tau;               /* > 0 and finite under FWM and FWM_UNTRUNC */
     int32_t calibration;     /* KIA_CAL_* */
     int32_t reconstruction;  /* KIA_REC_* */
     int32_t surrogate;       /* KIA_STE_* */

@@ -17,8 +17,8 @@ from dataclasses import dataclass
 from . import _lib
 from ._lib import KiaExt, KiaParams, KiaStatsLayout, KiaWorkspaceLayout
 
-CAL = {"minmax": 0, "fwm": 1}
-REC = {"lerp": 0, "nearest": 1}
+CAL = {"minmax": 0, "fwm": 1, "fwm_untrunc": 2}
+REC = {"lerp": 0, "nearest": 1, "exact": 2}
 STE = {"weight": 0, "prob": 1}
 RULE = {"full": 0, "detach": 1, "max_only": 2, "min_only": 3, "p1": 4}
 

@@ -19,11 +19,13 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 kia_status check_params(const kia_params* p) {
     if (!p) return KIA_ERR_NULL;
     if (p->n_intervals < 1 || p->n_intervals > kMaxIntervals) return KIA_ERR_PARAM;
-    if (p->calibration != KIA_CAL_MINMAX && p->calibration != KIA_CAL_FWM) return KIA_ERR_PARAM;
-    if (p->reconstruction != KIA_REC_LERP && p->reconstruction != KIA_REC_NEAREST) return KIA_ERR_PARAM;
+    if (p->calibration < KIA_CAL_MINMAX || p->calibration > KIA_CAL_FWM_UNTRUNC) return KIA_ERR_PARAM;
+    if (p->reconstruction < KIA_REC_LERP || p->reconstruction > KIA_REC_EXACT) return KIA_ERR_PARAM;
     if (p->surrogate != KIA_STE_WEIGHT && p->surrogate != KIA_STE_PROB) return KIA_ERR_PARAM;
     if (p->grad_rule < KIA_GRAD_FULL || p->grad_rule > KIA_GRAD_P1) return KIA_ERR_PARAM;
-    if (p->calibration == KIA_CAL_FWM && !(p->tau > 0.f && isfinite(p->tau))) return KIA_ERR_PARAM;
+    if (p->calibration != KIA_CAL_MINMAX && p->reconstruction != KIA_REC_EXACT &&
+        !(p->tau > 0.f && isfinite(p->tau)))
+        return KIA_ERR_PARAM;
     return KIA_OK;
 }
 
@@ -92,10 +94,15 @@ kia_status record(const kia_ext* ext, int i, hipStream_t st) {
     return hipEventRecord((hipEvent_t)ext->events[i], st) == hipSuccess ? KIA_OK : KIA_ERR_HIP;
 }
 
+// The exact-softmax reference is anchored at the row max only; it runs on the
+// FWM instantiation, whose grid constants it never reads.
+bool exact(const kia_params* p) { return p->reconstruction == KIA_REC_EXACT; }
+float tau_of(const kia_params* p) { return exact(p) ? 1.f : p->tau; }
+
 kia::FwdConfig config_of(const kia_params* p, int d, bool dump) {
     kia::FwdConfig c;
     c.d = d;
-    c.cal = p->calibration;
+    c.cal = exact(p) ? KIA_CAL_FWM : p->calibration;
     c.rec = p->reconstruction;
     c.prob = prob_extras(p);
     c.dump = dump;
@@ -171,7 +178,7 @@ kia_status kia_forward_ext(const kia_params* p, int B, int H, int T, int d, cons
     a.o_lerp = prob_extras(p) ? (float*)(base + L.o_lerp) : nullptr;
     a.idx_dump = ext ? ext->idx_dump : nullptr;
     a.BH = (int)s.BH; a.T = T; a.n_t = (int)s.n_t; a.K = p->n_intervals;
-    a.tau = p->tau;
+    a.tau = tau_of(p);
     a.scale = 1.f / sqrtf((float)d);
 
     hipStream_t hs = (hipStream_t)stream;
@@ -227,7 +234,7 @@ kia_status kia_backward_ext(const kia_params* p, int B, int H, int T, int d, con
     a.prefix_k = p1 ? (float*)(wb + WL.prefix_k) : nullptr;
     a.chunk_k = p1 ? (float*)(wb + WL.chunk_k) : nullptr;
     a.BH = (int)s.BH; a.T = T; a.n_t = (int)s.n_t; a.K = p->n_intervals;
-    a.tau = p->tau;
+    a.tau = tau_of(p);
     a.scale = 1.f / sqrtf((float)d);
     a.rule = p->grad_rule;
 

@@ -174,9 +174,18 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
                     const int key = k0 + acc_row(r, hl);
                     const bool valid = DIAG ? key <= qrow : true;
                     const float s = scur[r];
+                    if (REC == REC_EXACT) {
+                        // exact-softmax reference: P = exp(s - m) / W, direct term (dP - delta) P W / W_e
+                        const float pw = fast_exp2(fmaf(s - rg.m, kLog2e, lw));
+                        pr[r] = valid ? pw : 0.f;
+                        ds[r] = valid ? fmaf(dp[r], gW, ndW) * pw : 0.f;
+                        SA += ds[r];
+                        continue;
+                    }
                     const float u = (rg.m - s) * rg.invh;
-                    const bool keep = valid && ((CAL == CAL_MINMAX) ? true : (u <= rg.Kf));
-                    const float fi = fminf(floorf(u), rg.Kf - 1.f);
+                    const bool keep = valid && ((CAL == CAL_FWM) ? (u <= rg.Kf) : true);
+                    // the untruncated step continues the grid past K (no clamp)
+                    const float fi = (CAL == CAL_FWM_UNTRUNC) ? floorf(u) : fminf(floorf(u), rg.Kf - 1.f);
                     const float f = u - fi;
                     // G = dL/dw times the LERP segment's grid value g_i; the direct
                     // term and the h-derivative share it
@@ -194,10 +203,12 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
                     pr[r] = keep ? pw : 0.f;
                     ds[r] = keep ? G * rg.coh : 0.f;
                     SA += ds[r];
-                    // dL/dw * Wd with Wd / g = (c/h - 1) u + c f (i + 1)
-                    const float Gk = keep ? G : 0.f;
-                    SBu = fmaf(Gk, u, SBu);
-                    SBf = fmaf(Gk, fmaf(f, fi, f), SBf);
+                    if (CAL == CAL_MINMAX) {
+                        // dL/dw * Wd with Wd / g = (c/h - 1) u + c f (i + 1); only h = span/K needs it
+                        const float Gk = keep ? G : 0.f;
+                        SBu = fmaf(Gk, u, SBu);
+                        SBf = fmaf(Gk, fmaf(f, fi, f), SBf);
+                    }
                 }
             };
             if (kt == qt) grads(std::true_type{});
@@ -439,6 +450,10 @@ static hipError_t launch_rows_t(const BwdArgs& a, hipStream_t s) {
 
 template <int D, int CAL>
 static hipError_t launch_rows_rec(const FwdConfig& c, const BwdArgs& a, hipStream_t s) {
+    if (c.rec == REC_EXACT) {
+        if constexpr (CAL == CAL_FWM) return launch_rows_t<D, CAL, REC_EXACT, false>(a, s);
+        return hipErrorInvalidValue;
+    }
     if (c.rec == REC_LERP) return launch_rows_t<D, CAL, REC_LERP, false>(a, s);
     return c.prob ? launch_rows_t<D, CAL, REC_NEAREST, true>(a, s)
                   : launch_rows_t<D, CAL, REC_NEAREST, false>(a, s);
@@ -446,7 +461,9 @@ static hipError_t launch_rows_rec(const FwdConfig& c, const BwdArgs& a, hipStrea
 
 template <int D>
 static hipError_t launch_rows_d(const FwdConfig& c, const BwdArgs& a, hipStream_t s) {
-    return c.cal == CAL_MINMAX ? launch_rows_rec<D, CAL_MINMAX>(c, a, s) : launch_rows_rec<D, CAL_FWM>(c, a, s);
+    if (c.cal == CAL_MINMAX) return launch_rows_rec<D, CAL_MINMAX>(c, a, s);
+    if (c.cal == CAL_FWM) return launch_rows_rec<D, CAL_FWM>(c, a, s);
+    return launch_rows_rec<D, CAL_FWM_UNTRUNC>(c, a, s);
 }
 
 hipError_t launch_backward_rows(const FwdConfig& c, const BwdArgs& a, hipStream_t s) {

@@ -25,14 +25,15 @@ constexpr int kTile = 32;
 constexpr int kTileElems = kTile * kTile;
 constexpr int kWave = 64;
 
-enum { CAL_MINMAX = 0, CAL_FWM = 1 };
-enum { REC_LERP = 0, REC_NEAREST = 1 };
+enum { CAL_MINMAX = 0, CAL_FWM = 1, CAL_FWM_UNTRUNC = 2 };
+enum { REC_LERP = 0, REC_NEAREST = 1, REC_EXACT = 2 };
+
 enum { GRAD_FULL = 0, GRAD_DETACH = 1, GRAD_MAX_ONLY = 2, GRAD_MIN_ONLY = 3, GRAD_P1 = 4 };
 
 // Spans below this take the degenerate branch (App. A: branches for spans
 // above or below 1e-12).
 constexpr float kEpsSpan = 1e-12f;
-constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLog2e = 1.4426950408889634f;  // log2(e): exp(x) = exp2(x * log2(e))
 
 __device__ __forceinline__ f32x16 mfma32x32x2(float a, float b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -359,7 +360,7 @@ template <int CAL, bool NEED_NEAREST>
 __device__ __forceinline__ Recon reconstruct(const RowGrid& rg, float s) {
     Recon e;
     e.u = (rg.m - s) * rg.invh;
-    e.inwin = (CAL == CAL_MINMAX) ? true : (e.u <= rg.Kf);
+    e.inwin = (CAL == CAL_FWM) ? (e.u <= rg.Kf) : true;
     e.fi = fminf(floorf(e.u), rg.Kf - 1.f);
     e.f = e.u - e.fi;
     e.g = fast_exp2(-e.fi * rg.hl2);

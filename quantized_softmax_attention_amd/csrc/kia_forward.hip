@@ -226,9 +226,17 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
         const int key = kt_t * kTile + acc_row(r, hl);
         const bool valid = DIAG ? key <= qrow : true;
         const float s = sv[r];
+        if (REC == REC_EXACT) {
+            // exact-softmax reference: w = exp(s - m)
+            w[r] = valid ? fast_exp2((s - rg.m) * kLog2e) : 0.f;
+            Wt += w[r];
+            if (DUMP && qvalid && valid) a.idx_dump[((size_t)bh * T + qrow) * T + key] = 0;
+            return;
+        }
         const float u = (rg.m - s) * rg.invh;
-        const bool keep = valid && ((CAL == CAL_MINMAX) ? true : (u <= rg.Kf));
-        // unclamped segment: at u = K (the row min) the LERP value is g_K either way
+        const bool keep = valid && ((CAL == CAL_FWM) ? (u <= rg.Kf) : true);
+        // unclamped segment: at u = K (the row min) the LERP value is g_K either
+        // way, and the untruncated step continues the grid past K
         const float fi = floorf(u);
         const float g = fast_exp2(-fi * rg.hl2);
         const float wlv = g * fmaf(fi - u, rg.c, 1.f);
@@ -239,7 +247,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
         if (REC == REC_NEAREST) WLt += keep ? wlv : 0.f;
         if (PROB) wl[r] = keep ? wlv : 0.f;
         if (DUMP && qvalid && valid) {
-            int idx = (REC == REC_LERP) ? (int)fminf(fi, rg.Kf - 1.f) : (int)floorf(u + 0.5f);
+            int idx = (REC == REC_LERP) ? (CAL == CAL_FWM_UNTRUNC ? (int)fi : (int)fminf(fi, rg.Kf - 1.f))
+                                        : (int)floorf(u + 0.5f);
             if (!keep) idx = -1;
             a.idx_dump[((size_t)bh * T + qrow) * T + key] = idx;
         }
@@ -363,6 +372,13 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
 
 template <int D, int CAL>
 static hipError_t launch_fwd_rec(const FwdConfig& c, const FwdArgs& a, hipStream_t s) {
+    if (c.rec == REC_EXACT) {
+        // the exact reference is anchored at the max only: built on the FWM path
+        if constexpr (CAL == CAL_FWM)
+            return c.dump ? launch_fwd_t<D, CAL, REC_EXACT, false, true>(a, s)
+                          : launch_fwd_t<D, CAL, REC_EXACT, false, false>(a, s);
+        return hipErrorInvalidValue;
+    }
     if (c.rec == REC_LERP)
         return c.dump ? launch_fwd_t<D, CAL, REC_LERP, false, true>(a, s)
                       : launch_fwd_t<D, CAL, REC_LERP, false, false>(a, s);
@@ -375,7 +391,9 @@ static hipError_t launch_fwd_rec(const FwdConfig& c, const FwdArgs& a, hipStream
 
 template <int D>
 static hipError_t launch_fwd_d(const FwdConfig& c, const FwdArgs& a, hipStream_t s) {
-    return c.cal == CAL_MINMAX ? launch_fwd_rec<D, CAL_MINMAX>(c, a, s) : launch_fwd_rec<D, CAL_FWM>(c, a, s);
+    if (c.cal == CAL_MINMAX) return launch_fwd_rec<D, CAL_MINMAX>(c, a, s);
+    if (c.cal == CAL_FWM) return launch_fwd_rec<D, CAL_FWM>(c, a, s);
+    return launch_fwd_rec<D, CAL_FWM_UNTRUNC>(c, a, s);
 }
 
 hipError_t launch_forward(const FwdConfig& c, const FwdArgs& a, hipStream_t s) {

@@ -28,8 +28,8 @@ ZERO_SUM_TOL = 1e-5
 
 
 def to_oracle_params(p):
-    cal = {"minmax": O.MINMAX, "fwm": O.FWM}[p.calibration]
-    rec = {"lerp": O.LERP, "nearest": O.NEAREST}[p.reconstruction]
+    cal = {"minmax": O.MINMAX, "fwm": O.FWM, "fwm_untrunc": O.FWM_UNTRUNC}[p.calibration]
+    rec = {"lerp": O.LERP, "nearest": O.NEAREST, "exact": O.EXACT}[p.reconstruction]
     ste = {"weight": O.WEIGHT_STE, "prob": O.PROB_STE}[p.surrogate]
     rule = {"full": O.FULL, "detach": O.DETACH, "max_only": O.MAX_ONLY, "min_only": O.MIN_ONLY,
             "p1": O.P1}[p.grad_rule]
@@ -179,15 +179,17 @@ class SliceCheck:
             if t >= 1:
                 if srt[-1] - srt[-2] <= tie_band:
                     ab_amb = True
-                if p.calibration == O.MINMAX and srt[1] - srt[0] <= tie_band:
+                if p.calibration == O.MINMAX and p.reconstruction != O.EXACT and srt[1] - srt[0] <= tie_band:
                     ab_amb = True
             if not ab_amb:
-                assert g["a"][t] == cal.a, (t, g["a"][t], cal.a)
-                if p.calibration == O.MINMAX:
-                    assert g["b"][t] == cal.b, (t, g["b"][t], cal.b)
-            if cal.degenerate or t == 0:
+                assert g["a"][t] == cal.a, ("argmax", t, g["a"][t], cal.a)
+                if p.calibration == O.MINMAX and p.reconstruction != O.EXACT:
+                    assert g["b"][t] == cal.b, ("argmin", t, g["b"][t], cal.b)
+            if cal.degenerate or t == 0 or p.reconstruction == O.EXACT:
                 if ab_amb:
                     self.amb_bwd[t] = True
+                    if p.reconstruction == O.EXACT:
+                        self.amb_keys_bwd.update(range(t + 1))
                 continue
             # decision band in grid steps
             mg, ng = float(g["m"][t]), float(g["n"][t])
@@ -195,9 +197,13 @@ class SliceCheck:
             u_ref = fw.rec.u
             u_pred = (mg - sg) / hg if sg is not None else u_ref
             band = 2 * (np.abs(u_pred - u_ref) + 4 * 2.0 ** -24 * (np.abs(u_ref) + 1))
-            uc = np.minimum(u_ref, K)
+            untrunc = p.calibration == O.FWM_UNTRUNC
+            uc = u_ref if untrunc else np.minimum(u_ref, K)
             knot = np.abs(uc - np.round(uc)) <= band                 # LERP segment boundaries
-            knot &= (uc > band) & (uc < K - band)                      # u = 0 / u = K are exact (max/min keys)
+            if untrunc:
+                knot &= uc > band                                      # the grid continues past K
+            else:
+                knot &= (uc > band) & (uc < K - band)                  # u = 0 / u = K are exact (max/min keys)
             edge = (np.abs(u_ref - K) <= band) if p.calibration == O.FWM else np.zeros_like(knot)
             half = np.abs(uc - (np.floor(uc) + 0.5)) <= band if p.reconstruction == O.NEAREST \
                 else np.zeros_like(knot)
@@ -214,8 +220,9 @@ class SliceCheck:
                         jumps.append(fw.rec.g[K])
                     else:
                         r = int(np.floor(uc[j] + 0.5))
-                        lo, hi = max(r - 1, 0), min(r + 1, K)
-                        jumps.append(max(abs(fw.rec.g[r] - fw.rec.g[lo]), abs(fw.rec.g[hi] - fw.rec.g[r])))
+                        lo, hi = max(r - 1, 0), (r + 1 if untrunc else min(r + 1, K))
+                        gv = lambda x: float(np.exp(-fw.cal.h * x))
+                        jumps.append(max(abs(gv(r) - gv(lo)), abs(gv(hi) - gv(r))))
                 rel = max(jumps) / fw.W
                 if rel > 1e-7:
                     self.amb_fwd[t] = True

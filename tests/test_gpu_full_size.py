@@ -33,16 +33,19 @@ def P(**kw):
     return Params(**kw)
 
 
-def zero_sum_all_rows(g, tol=1e-5):
+def zero_sum_all_rows(g, params, tol=1e-5):
     """Rows of the GPU's dS (calibration terms folded in) whose |sum| exceeds
-    tol * L1, over every row of every slice; rows whose stored span is below
-    the degenerate threshold are skipped (single-key rows have dS = 0)."""
+    tol * L1, over every row of every slice.  Under MinMax, rows whose stored
+    span is below the degenerate threshold are skipped (their softmax-limit
+    gradient cancels only to the rounding of two dot products; single-key rows
+    have dS = 0 and pass anyway)."""
     import torch
     dS = g["dS"]
-    span = (g["m"] - g["n"]).double()
     sums = dS.double().sum(-1)
     l1 = dS.double().abs().sum(-1)
-    bad = (sums.abs() > tol * l1) & (span >= 1e-12)
+    bad = sums.abs() > tol * l1
+    if params.calibration == "minmax" and params.reconstruction != "exact":
+        bad &= (g["m"] - g["n"]).double() >= 1e-12
     idx = torch.nonzero(bad)[:5].tolist()
     detail = [(tuple(i), float(sums[tuple(i)]), float(l1[tuple(i)]), int(g["a"][tuple(i)]), int(g["b"][tuple(i)]),
                float(g["cm"][tuple(i)]), float(g["cn"][tuple(i)])) for i in idx]
@@ -71,7 +74,7 @@ def full_check(name, params, heads, rows=None, tail=None, zero_sum=None):
         ties += int(sc.amb_bwd.sum())
         excluded += sc.n_amb_pairs
     if zero_sum if zero_sum is not None else params.grad_rule in ("full", "p1"):
-        nbad, nrows, detail = zero_sum_all_rows(g)
+        nbad, nrows, detail = zero_sum_all_rows(g, params)
         assert nbad == 0, f"{nbad} of {nrows} rows violate the zero row sum: (b,h,t), sum, L1, a, b, cm, cn = {detail}"
         print(f"  zero row sum holds on all {nrows} rows", flush=True)
     print(f"  worst rel err {worst}; rows with a boundary-near decision {ties}; "
@@ -96,6 +99,23 @@ def test_c2_full_size_p1(K):
     """P1 (zero-sum projection of the detached gradient) at full size."""
     full_check("c2", P(K=K, calibration="minmax", reconstruction="lerp", grad_rule="p1"),
                _heads(13 + K, WORKLOADS["c2"]))
+
+
+@pytest.mark.parametrize("rec,ste", [("lerp", "weight"), ("nearest", "prob")])
+def test_c2_full_size_untruncated_step(rec, ste):
+    """The untruncated fixed step (FWM's step without the zero tail) at full size."""
+    full_check("c2", P(K=4, tau=6.0, calibration="fwm_untrunc", reconstruction=rec, surrogate=ste),
+               _heads(21 if rec == "lerp" else 22, WORKLOADS["c2"]))
+
+
+@pytest.mark.parametrize("rule", ["full", "detach"])
+def test_c2_full_size_exact_softmax(rule):
+    """The exact-softmax reference on the same kernels at full size.  Only the
+    full rule folds the calibration term into the argmax entry, which is what
+    makes each row sum exact; under detach the direct terms cancel only to the
+    rounding of delta = dO.O, so the row-sum bar applies to the full rule."""
+    full_check("c2", P(K=1, reconstruction="exact", grad_rule=rule), _heads(30, WORKLOADS["c2"]),
+               zero_sum=(rule == "full"))
 
 
 @pytest.mark.parametrize("cal", ["minmax", "fwm"])

@@ -54,7 +54,9 @@ SMALL128 = Workload("small_ragged_d128", 1, 2, 75, 128, "head_temp", lo=0.5, hi=
 
 COMBOS = [("minmax", "lerp", "weight"), ("fwm", "lerp", "weight"),
           ("minmax", "nearest", "weight"), ("minmax", "nearest", "prob"),
-          ("fwm", "nearest", "weight"), ("fwm", "nearest", "prob")]
+          ("fwm", "nearest", "weight"), ("fwm", "nearest", "prob"),
+          ("fwm_untrunc", "lerp", "weight"), ("fwm_untrunc", "nearest", "weight"),
+          ("fwm_untrunc", "nearest", "prob"), ("minmax", "exact", "weight")]
 RULES = ["full", "detach", "max_only", "min_only", "p1"]
 
 

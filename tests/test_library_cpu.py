@@ -100,7 +100,7 @@ def _bwd(lib, p, ptrs=None, nbytes=1 << 40, wbytes=1 << 40, T=8, d=64):
     return lib.kia_backward(ctypes.byref(p), 1, 1, T, d, q, k, v, o, do, st, nbytes, dq, dk, dv, ws, wbytes, None)
 
 
-@pytest.mark.parametrize("field,value", [("n_intervals", 0), ("n_intervals", 65537), ("calibration", 2),
+@pytest.mark.parametrize("field,value", [("n_intervals", 0), ("n_intervals", 65537), ("calibration", 3),
                                          ("reconstruction", -1), ("surrogate", 3), ("grad_rule", 5)])
 def test_bad_params_rejected(field, value):
     lib, mod = _lib()
