@@ -5,7 +5,8 @@ and the benchmark's CPU-baseline leg, never by the HIP library or its
 binding.  It shares no code with them.
 """
 from .kia_oracle import (  # noqa: F401
-    DETACH, EPS_SPAN, EXACT, FULL, FWM, FWM_UNTRUNC, LERP, MAX_ONLY, MIN_ONLY, MINMAX, NEAREST, P1,
-    PROB_STE, WEIGHT_STE, Params, backward, calibrate, forward, grid, head_backward,
-    head_forward, reconstruct, row_backward, row_forward, row_scores,
+    DETACH, EPS_SPAN, EXACT, FULL, FWM, FWM_UNTRUNC, GEOMETRY_FIELDS, LERP, MAX_ONLY, MIN_ONLY,
+    MINMAX, NEAREST, P1, PROB_STE, WEIGHT_STE, Params, backward, calibrate, forward, geometry, grid,
+    head_backward, head_forward, head_geometry, reconstruct, row_backward, row_forward, row_geometry,
+    row_scores,
 )

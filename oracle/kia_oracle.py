@@ -54,6 +54,16 @@ Readings where the pages leave a step open (each is listed in the design doc):
       operator against softmax): w = exp(s - m); the calibration and
       surrogate flags are ignored; its calibration term through m vanishes
       up to rounding, so every rule gives the softmax gradient P (dP - delta).
+  R13 The geometry probe (section 4 "Geometry probe"; section 5.4; App. D.6)
+      reports per causal row: the span max - min; the native width, i.e. the
+      interval width h the operator lays on the row (MinMax span/K, 0 in the
+      degenerate branch; FWM and the untruncated step tau/K; the exact
+      reference has no grid of its own and reports the MinMax width of the
+      given K); the norms |Q_t| and |K_t| of the unscaled projections; the
+      entropies (nats) of the operator's forward probabilities P and of the
+      softmax of the same scores; their total variation (1/2) sum |P - softmax|;
+      and the softmax mass of the top rounding bucket, the keys whose Nearest
+      point on that grid is 0 (u = (m - s)/h < 1/2; every key when h = 0).
 
 Parity: every function below is pinned by the CPU tests (closed forms,
 brute force, finite differences, an autograd re-expression, the softmax
@@ -367,4 +377,81 @@ def backward(q, k, v, do, p: Params):
             r = head_backward(q[bi, hi], k[bi, hi], v[bi, hi], do[bi, hi], p)
             for key in out:
                 out[key][bi, hi] = r[key]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# geometry probe (reading R13)
+# ---------------------------------------------------------------------------
+
+@dataclass
+class RowGeometry:
+    span: float          # max - min over the causal keys
+    h: float             # native width: the operator's interval width
+    entropy_p: float     # entropy of the operator's probabilities (nats)
+    entropy_soft: float  # entropy of the softmax of the same scores
+    tv: float            # total variation between the two
+    top_mass: float      # softmax mass whose Nearest point on the grid is 0
+
+
+GEOMETRY_FIELDS = ("span", "h", "q_norm", "k_norm", "entropy_p", "entropy_soft", "tv", "top_mass")
+
+
+def _entropy(P: np.ndarray) -> float:
+    nz = P[P > 0]
+    return float(-(nz * np.log(nz)).sum())
+
+
+def row_geometry(s: np.ndarray, p: Params) -> RowGeometry:
+    """Score geometry of one causal row (section 4 "Geometry probe";
+    section 5.4; App. D.6; reading R13)."""
+    fw = row_forward(s, p)
+    m, n = float(s.max()), float(s.min())
+    span = m - n
+    if p.calibration in (FWM, FWM_UNTRUNC) and p.reconstruction != EXACT:
+        h = p.tau / p.K
+    else:
+        h = span / p.K if span >= EPS_SPAN else 0.0
+    e = np.exp(s - m)
+    soft = e / e.sum()
+    if h > 0:
+        top = (m - s) / h < 0.5
+    else:
+        top = np.ones(s.shape, dtype=bool)
+    return RowGeometry(
+        span=span,
+        h=h,
+        entropy_p=_entropy(fw.P),
+        entropy_soft=_entropy(soft),
+        tv=0.5 * float(np.abs(fw.P - soft).sum()),
+        top_mass=float(soft[top].sum()),
+    )
+
+
+def head_geometry(Q, Kt, p: Params, rows=None):
+    """Geometry probe over one head ([T, d] inputs): a dict of [T] arrays
+    named by GEOMETRY_FIELDS (rows not asked for are NaN)."""
+    T, d = Q.shape
+    rows = range(T) if rows is None else rows
+    out = {f: np.full(T, np.nan) for f in GEOMETRY_FIELDS}
+    Q64, K64 = Q.astype(np.float64), Kt.astype(np.float64)
+    for t in rows:
+        g = row_geometry(row_scores(Q64[t], K64[: t + 1]), p)
+        out["span"][t], out["h"][t] = g.span, g.h
+        out["q_norm"][t] = np.sqrt((Q64[t] ** 2).sum())
+        out["k_norm"][t] = np.sqrt((K64[t] ** 2).sum())
+        out["entropy_p"][t], out["entropy_soft"][t] = g.entropy_p, g.entropy_soft
+        out["tv"][t], out["top_mass"][t] = g.tv, g.top_mass
+    return out
+
+
+def geometry(q, k, p: Params):
+    """Geometry probe over [B, H, T, d] inputs: a dict of [B, H, T] arrays."""
+    B, H, T, d = q.shape
+    out = {f: np.zeros((B, H, T)) for f in GEOMETRY_FIELDS}
+    for bi in range(B):
+        for hi in range(H):
+            r = head_geometry(q[bi, hi], k[bi, hi], p)
+            for f in GEOMETRY_FIELDS:
+                out[f][bi, hi] = r[f]
     return out
