@@ -238,6 +238,7 @@ def main():
     ap.add_argument("--cpu-slices", type=int, default=96,
                     help="oracle sample size for the CPU baseline, in (b, h) slices (capped at B*H)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true", help="skip timing the geometry probe")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--ingest-pmc", metavar="DIR",
@@ -329,6 +330,30 @@ def main():
     dominant = max(("forward", "backward_rows", "backward_cols"), key=lambda n: kern_ms[n])
     achieved = flop_kernel / (kern_ms[dominant] * 1e-3) / 1e12
 
+    # the geometry probe, timed on its own after the steps (not part of a
+    # step): one row reduction over the score tiles the last forward stored
+    probe = None
+    if not args.no_probe:
+        geo = torch.empty((8, B, H, T), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            kia.kia_geometry(tq, tk, stats, params, geo=geo)
+        pe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for a, b in pe:
+            a.record()
+            kia.kia_geometry(tq, tk, stats, params, geo=geo)
+            b.record()
+        torch.cuda.synchronize()
+        probe_ms = float(np.mean([a.elapsed_time(b) for a, b in pe]))
+        n_t = (T + 31) // 32
+        probe_bytes = (B * H * (n_t * (n_t + 1) // 2) * 4096      # score tiles
+                       + 2 * B * H * T * d * 4                     # Q, K rows (norms)
+                       + 2 * B * H * T * 4 + 8 * B * H * T * 4)    # row max, W in; 8 fields out
+        gbps = probe_bytes / (probe_ms * 1e-3) / 1e9
+        probe = {"kernel": "geometry", "bound": "hbm", "avg_ms": round(probe_ms, 4),
+                 "bytes_per_launch": probe_bytes, "achieved": round(gbps, 1), "peak": PEAK_HBM,
+                 "unit": "GB/s", "frac": round(gbps / PEAK_HBM, 4)}
+
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         try:
@@ -365,6 +390,8 @@ def main():
                      "avg_ms": round(kern_ms[dominant], 4)},
         "kernel_ms": {n: round(t, 4) for n, t in kern_ms.items()},
     }
+    if probe is not None:
+        out["geometry_probe"] = probe
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)

@@ -168,6 +168,37 @@ kia_status kia_backward_ext(const kia_params* p, int B, int H, int T, int d,
                             float* dq, float* dk, float* dv,
                             void* ws, size_t ws_bytes, void* stream, const kia_ext* ext);
 
+/* Score-geometry probe ("Pretraining Transformers with Quantized Softmax in
+ * Attention", section 4 "Geometry probe"; section 5.4; App. D.6): per causal
+ * row, statistics of the learned scores and of the operator's distortion of
+ * the softmax, reduced from the score tiles a kia_forward call with the same
+ * params and shape left in `stats` (q and k are that call's inputs; `stats`
+ * is only read).  `geo` (device, fp32, 16-byte aligned, caller-owned, at least
+ * kia_geometry_bytes(B, H, T) bytes) receives KIA_GEO_FIELDS arrays of B*H*T
+ * values, field f of row (b, h, t) at geo[f * B*H*T + (b*H + h)*T + t]:
+ *   SPAN      max - min of the row's scores
+ *   WIDTH     the interval width h the operator lays on the row (MinMax
+ *             span/K, 0 on rows below the degenerate span; FWM and
+ *             FWM_UNTRUNC tau/K; under KIA_REC_EXACT the MinMax width span/K)
+ *   Q_NORM    |Q_t|, K_NORM |K_t| (unscaled projections at position t)
+ *   ENTROPY_P entropy (nats) of the operator's probabilities P
+ *   ENTROPY_S entropy of the softmax of the same scores
+ *   TV        total variation (1/2) sum_j |P_j - softmax_j|
+ *   TOP_MASS  softmax mass of the top rounding bucket: keys whose Nearest
+ *             point on that grid is 0, i.e. u = (max - s)/h < 1/2 (every key
+ *             when the width is 0).
+ * Reductions accumulate in fp32 within a 32-key tile and in fp64 across
+ * tiles.  Errors as for kia_forward; KIA_ERR_BUFFER if `geo_bytes` is short.
+ * Nothing is written for padding rows. */
+enum {
+    KIA_GEO_SPAN = 0, KIA_GEO_WIDTH = 1, KIA_GEO_Q_NORM = 2, KIA_GEO_K_NORM = 3,
+    KIA_GEO_ENTROPY_P = 4, KIA_GEO_ENTROPY_S = 5, KIA_GEO_TV = 6, KIA_GEO_TOP_MASS = 7,
+    KIA_GEO_FIELDS = 8
+};
+size_t kia_geometry_bytes(int B, int H, int T);
+kia_status kia_geometry(const kia_params* p, int B, int H, int T, int d, const float* q, const float* k,
+                        const void* stats, size_t stats_bytes, float* geo, size_t geo_bytes, void* stream);
+
 /* Expand a tile buffer (scores from stats, or probs / dscores from the
  * workspace) into a dense fp32 [B,H,T,T] matrix for inspection.  key_major:
  * 0 for the score tiles, 1 for the workspace tiles.  Only causal entries are

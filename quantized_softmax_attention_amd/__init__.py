@@ -167,6 +167,27 @@ def kia_backward(q, k, v, o, do, stats, params: Params, dq=None, dk=None, dv=Non
     return dq, dk, dv, ws
 
 
+GEOMETRY_FIELDS = ("span", "h", "q_norm", "k_norm", "entropy_p", "entropy_soft", "tv", "top_mass")
+
+
+def kia_geometry(q, k, stats, params: Params, geo=None, stream=None):
+    """Score-geometry probe over the scores a kia_forward call with the same
+    params left in stats.  Returns geo, fp32 [8, B, H, T], fields in the
+    order of GEOMETRY_FIELDS."""
+    torch = _torch()
+    B, H, T, d = _shape(q)
+    _check(k, "k", (B, H, T, d))
+    lib = _lib.load()
+    if geo is None:
+        geo = torch.empty((len(GEOMETRY_FIELDS), B, H, T), dtype=torch.float32, device=q.device)
+    _check(geo, "geo")
+    st = lib.kia_geometry(ctypes.byref(params.c()), B, H, T, d, q.data_ptr(), k.data_ptr(), stats.data_ptr(),
+                          stats.numel(), geo.data_ptr(), geo.numel() * geo.element_size(), _stream(stream))
+    if st:
+        raise KiaError(st, "kia_geometry")
+    return geo
+
+
 def kia_tiles_to_dense(B, H, T, tiles, key_major: bool, dense=None, stream=None):
     """Expand a tile buffer (a uint8/float view starting at the tiles) into a
     dense [B, H, T, T] fp32 tensor; non-causal entries keep dense's content
@@ -187,4 +208,4 @@ def kia_abi_version() -> int:
 
 __all__ = ["Params", "KiaError", "kia_forward", "kia_backward", "kia_stats_bytes",
            "kia_workspace_bytes", "kia_stats_layout_query", "kia_workspace_layout_query",
-           "kia_tiles_to_dense", "kia_abi_version"]
+           "kia_geometry", "GEOMETRY_FIELDS", "kia_tiles_to_dense", "kia_abi_version"]

@@ -48,6 +48,8 @@ SIGNATURES = {
     "kia_forward_ext": (c_int, [P] + _SHAPE + [c_void_p] * 5 + [c_size_t, c_void_p, POINTER(KiaExt)]),
     "kia_backward_ext": (c_int, [P] + _SHAPE + [c_void_p] * 6 + [c_size_t] + [c_void_p] * 4
                          + [c_size_t, c_void_p, POINTER(KiaExt)]),
+    "kia_geometry_bytes": (c_size_t, [c_int, c_int, c_int]),
+    "kia_geometry": (c_int, [P] + _SHAPE + [c_void_p] * 3 + [c_size_t, c_void_p, c_size_t, c_void_p]),
     "kia_tiles_to_dense": (c_int, [c_int, c_int, c_int, c_void_p, c_int, c_void_p, c_void_p]),
     "kia_status_str": (c_char_p, [c_int]),
     "kia_abi_version": (c_int32, []),

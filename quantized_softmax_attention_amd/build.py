@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkia.so")
-SOURCES = ["kia_api.hip", "kia_forward.hip", "kia_backward.hip", "kia_p1.hip"]
+SOURCES = ["kia_api.hip", "kia_forward.hip", "kia_backward.hip", "kia_p1.hip", "kia_geometry.hip"]
 
 ARCH = "gfx950"
 HIPCC_FLAGS = [

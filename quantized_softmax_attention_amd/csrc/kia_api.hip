@@ -257,6 +257,40 @@ kia_status kia_backward(const kia_params* p, int B, int H, int T, int d, const f
                             stream, nullptr);
 }
 
+size_t kia_geometry_bytes(int B, int H, int T) {
+    if (B < 1 || H < 1 || T < 1) return 0;
+    const double n = (double)B * H * T * KIA_GEO_FIELDS * 4.0;
+    if (n > 9.0e18) return 0;
+    return (size_t)B * H * T * KIA_GEO_FIELDS * 4;
+}
+
+kia_status kia_geometry(const kia_params* p, int B, int H, int T, int d, const float* q, const float* k,
+                        const void* stats, size_t stats_bytes, float* geo, size_t geo_bytes, void* stream) {
+    kia_status st = check_params(p);
+    if (st != KIA_OK) return st;
+    Shape s;
+    if ((st = check_shape(B, H, T, d, &s)) != KIA_OK) return st;
+    if (!q || !k || !stats || !geo) return KIA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(stats) || !aligned16(geo)) return KIA_ERR_ALIGN;
+    kia_stats_layout L;
+    stats_layout(p, s, &L);
+    if (stats_bytes < L.total_bytes) return KIA_ERR_BUFFER;
+    if (geo_bytes < kia_geometry_bytes(B, H, T)) return KIA_ERR_BUFFER;
+
+    const char* sb = (const char*)stats;
+    kia::GeoArgs a;
+    a.q = q; a.k = k;
+    a.tiles = (const float*)(sb + L.scores);
+    a.row_m = (const float*)(sb + L.row_m);
+    a.row_w = (const float*)(sb + L.row_w);
+    a.geo = geo;
+    a.BH = (int)s.BH; a.T = T; a.n_t = (int)s.n_t; a.K = p->n_intervals; a.d = d;
+    a.tau = p->tau;
+    return kia::launch_geometry(p->calibration, p->reconstruction, a, (hipStream_t)stream) == hipSuccess
+               ? KIA_OK
+               : KIA_ERR_HIP;
+}
+
 kia_status kia_tiles_to_dense(int B, int H, int T, const float* tiles, int key_major, float* dense,
                               void* stream) {
     if (!tiles || !dense) return KIA_ERR_NULL;
@@ -284,6 +318,6 @@ const char* kia_status_str(kia_status s) {
     return "unknown status";
 }
 
-int32_t kia_abi_version(void) { return 2; }
+int32_t kia_abi_version(void) { return 3; }
 
 }  // extern "C"

@@ -34,6 +34,7 @@ enum { GRAD_FULL = 0, GRAD_DETACH = 1, GRAD_MAX_ONLY = 2, GRAD_MIN_ONLY = 3, GRA
 // above or below 1e-12).
 constexpr float kEpsSpan = 1e-12f;
 constexpr float kLog2e = 1.4426950408889634f;  // log2(e): exp(x) = exp2(x * log2(e))
+constexpr float kLn2 = 0.6931471805599453f;    // ln(2): ln(exp2(x)) = x * ln(2)
 
 __device__ __forceinline__ f32x16 mfma32x32x2(float a, float b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);

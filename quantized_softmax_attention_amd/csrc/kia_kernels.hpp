@@ -52,6 +52,17 @@ struct BwdArgs {
     int rule;
 };
 
+struct GeoArgs {
+    const float* q;
+    const float* k;
+    const float* tiles;  // score tiles of a forward with the same flags
+    const float* row_m;
+    const float* row_w;
+    float* geo;          // [8][BH * T]
+    int BH, T, n_t, K, d;
+    float tau;
+};
+
 struct FwdConfig {
     int d, cal, rec;
     bool prob, dump;
@@ -62,6 +73,7 @@ hipError_t launch_backward_rows(const FwdConfig& c, const BwdArgs& a, hipStream_
 hipError_t launch_backward_cols(int d, const BwdArgs& a, hipStream_t s);
 hipError_t launch_key_prefix(int d, const BwdArgs& a, hipStream_t s);
 hipError_t launch_center_rows(const BwdArgs& a, hipStream_t s);
+hipError_t launch_geometry(int cal, int rec, const GeoArgs& a, hipStream_t s);
 hipError_t launch_tiles_to_dense(int BH, int T, const float* tiles, int key_major, float* dense,
                                  hipStream_t s);
 

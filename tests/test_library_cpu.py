@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), f"libkia.so does not export {name}"
         assert name in mod.SIGNATURES, f"binding has no signature for {name}"
     assert set(mod.SIGNATURES) == set(names)
-    assert lib.kia_abi_version() == 2
+    assert lib.kia_abi_version() == 3
 
 
 def _params(mod, K=4, tau=6.0, cal=0, rec=0, ste=0, rule=0):
@@ -142,6 +142,27 @@ def test_null_misaligned_and_small_buffers_rejected():
         assert _bwd(lib, p, bad) == 4
     assert _bwd(lib, p, wbytes=64) == 5
     assert _bwd(lib, p, nbytes=64) == 5
+
+
+def test_geometry_probe_size_and_argument_checks():
+    lib, mod = _lib()
+    p = _params(mod)
+    assert lib.kia_geometry_bytes(2, 3, 100) == 8 * 2 * 3 * 100 * 4
+    assert lib.kia_geometry_bytes(0, 3, 100) == 0
+    B, H, T, d = 1, 2, 40, 64
+    nbytes = lib.kia_stats_bytes(p, B, H, T, d)
+    gbytes = lib.kia_geometry_bytes(B, H, T)
+
+    def geo(p=p, q=A, k=A, stats=A, sb=nbytes, g=A, gb=gbytes, T=T, d=d):
+        return lib.kia_geometry(p, B, H, T, d, q, k, stats, sb, g, gb, None)
+
+    assert geo(p=None) == 1
+    assert geo(q=0) == 1 and geo(k=0) == 1 and geo(stats=0) == 1 and geo(g=0) == 1
+    assert geo(g=A + 4) == 4 and geo(stats=A + 8) == 4
+    assert geo(sb=nbytes - 1) == 5
+    assert geo(gb=gbytes - 4) == 5
+    assert geo(d=96) == 2 and geo(T=0) == 2
+    assert geo(p=_params(mod, cal=1, tau=0.0)) == 3
 
 
 def test_status_strings():
