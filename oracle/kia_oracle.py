@@ -54,12 +54,22 @@ Readings where the pages leave a step open (each is listed in the design doc):
       operator against softmax): w = exp(s - m); the calibration and
       surrogate flags are ignored; its calibration term through m vanishes
       up to rounding, so every rule gives the softmax gradient P (dP - delta).
+  R14 The reduced-precision exponential baselines (App. D.5, Table S11):
+      exact softmax with each exp(s - m) rounded, before normalisation, to
+      bf16 (BF16-exp) or to FP8 (FP8-exp), round to nearest, ties to even.
+      The pages do not name the FP8 format; the forward-pass format E4M3
+      (OCP: 3 fraction bits, exponent bias 7, subnormal step 2^-9) is taken.
+      The backward is straight-through: the rounding counts as the identity,
+      so dS_direct = gt * exp(s - m) with gt = (dP - delta)/W evaluated at the
+      rounded P and W; the shift m carries -sum(dS_direct) to the argmax under
+      full and max-only.  The calibration, tau and surrogate flags are
+      ignored, as for the exact reference.
   R13 The geometry probe (section 4 "Geometry probe"; section 5.4; App. D.6)
       reports per causal row: the span max - min; the native width, i.e. the
       interval width h the operator lays on the row (MinMax span/K, 0 in the
       degenerate branch; FWM and the untruncated step tau/K; the exact
       reference has no grid of its own and reports the MinMax width of the
-      given K); the norms |Q_t| and |K_t| of the unscaled projections; the
+      given K, and so do the rounded-exponential baselines); the norms |Q_t| and |K_t| of the unscaled projections; the
       entropies (nats) of the operator's forward probabilities P and of the
       softmax of the same scores; their total variation (1/2) sum |P - softmax|;
       and the softmax mass of the top rounding bucket, the keys whose Nearest
@@ -76,7 +86,8 @@ from dataclasses import dataclass
 import numpy as np
 
 MINMAX, FWM, FWM_UNTRUNC = 0, 1, 2
-LERP, NEAREST, EXACT = 0, 1, 2
+LERP, NEAREST, EXACT, EXP_BF16, EXP_FP8 = 0, 1, 2, 3, 4
+EXP_FAMILY = (EXACT, EXP_BF16, EXP_FP8)   # softmax anchored at the max, no grid
 WEIGHT_STE, PROB_STE = 0, 1
 FULL, DETACH, MAX_ONLY, MIN_ONLY, P1 = 0, 1, 2, 3, 4
 
@@ -96,7 +107,8 @@ class Params:
         return self.grad_rule in (FULL, MAX_ONLY)
 
     def carries_min(self) -> bool:
-        return self.grad_rule in (FULL, MIN_ONLY) and self.calibration == MINMAX and self.reconstruction != EXACT
+        return (self.grad_rule in (FULL, MIN_ONLY) and self.calibration == MINMAX
+                and self.reconstruction not in EXP_FAMILY)
 
 
 # ---------------------------------------------------------------------------
@@ -126,7 +138,7 @@ def calibrate(s: np.ndarray, p: Params) -> Calibration:
     a = int(np.argmax(s))   # numpy returns the first maximal index
     b = int(np.argmin(s))
     m, n = float(s[a]), float(s[b])
-    if p.calibration == MINMAX and p.reconstruction != EXACT:
+    if p.calibration == MINMAX and p.reconstruction not in EXP_FAMILY:
         span = m - n
         if span < EPS_SPAN:
             return Calibration(m, a, n, b, 0.0, True)
@@ -185,6 +197,21 @@ def reconstruct(s: np.ndarray, m: float, h: float, p: Params, clamp: bool = True
     return Recon(u, uc, mask, i, f, r, g, gi, gi1, wL, wN)
 
 
+def round_to_format(x: np.ndarray, frac_bits: int, emin: int) -> np.ndarray:
+    """Round non-negative values to nearest, ties to even, in a binary
+    floating-point format with `frac_bits` fraction bits and smallest normal
+    exponent `emin` (gradual underflow below 2^emin; the values rounded here
+    are at most 1, so the format's top end never matters).  bf16: 7, -126;
+    FP8 E4M3: 3, -6 (R14)."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)                        # x = f 2^e with f in [1/2, 1)
+    quantum = np.ldexp(1.0, np.maximum(e - 1, emin) - frac_bits)
+    return np.rint(x / quantum) * quantum      # np.rint rounds ties to even
+
+
+FORMATS = {EXP_BF16: (7, -126), EXP_FP8: (3, -6)}
+
+
 @dataclass
 class RowForward:
     s: np.ndarray
@@ -199,8 +226,10 @@ class RowForward:
 
 def row_forward(s: np.ndarray, p: Params) -> RowForward:
     cal = calibrate(s, p)
-    if p.reconstruction == EXACT:                               # R12: exact softmax
+    if p.reconstruction in EXP_FAMILY:                         # R12, R14: softmax
         w = np.exp(s - cal.m)
+        if p.reconstruction in FORMATS:
+            w = round_to_format(w, *FORMATS[p.reconstruction])
         W = float(w.sum())
         return RowForward(s, cal, None, w, W, w / W, w, W)
     if cal.degenerate:                                          # R4
@@ -228,11 +257,12 @@ class RowBackward:
 def row_backward(fw: RowForward, dP: np.ndarray, p: Params) -> RowBackward:
     """Score gradient of one row given dP_j = dO_t . V_j (App. B)."""
     cal, rec = fw.cal, fw.rec
-    if p.reconstruction == EXACT:                               # R12
+    if p.reconstruction in EXP_FAMILY:                         # R12, R14
         delta = float(np.dot(fw.P, dP))
         gt = (dP - delta) / fw.W
-        dS_direct = gt * fw.w                                   # d exp(s - m) / ds
-        Cm = -float(np.sum(gt * fw.w))                          # through the shift m (0 up to rounding)
+        e = np.exp(fw.s - cal.m)                                # straight through any rounding
+        dS_direct = gt * e                                      # d exp(s - m) / ds
+        Cm = -float(np.sum(gt * e))                             # through the shift m
         dS = dS_direct.copy()
         if p.grad_rule == P1:
             dS = dS - dS.mean()
@@ -408,7 +438,7 @@ def row_geometry(s: np.ndarray, p: Params) -> RowGeometry:
     fw = row_forward(s, p)
     m, n = float(s.max()), float(s.min())
     span = m - n
-    if p.calibration in (FWM, FWM_UNTRUNC) and p.reconstruction != EXACT:
+    if p.calibration in (FWM, FWM_UNTRUNC) and p.reconstruction not in EXP_FAMILY:
         h = p.tau / p.K
     else:
         h = span / p.K if span >= EPS_SPAN else 0.0

@@ -24,8 +24,13 @@ def surrogate_objective(mod, s, s0, dP, p):
     live_min = p.grad_rule in (mod.FULL, mod.MIN_ONLY)
     m = s.max() if live_max else cal0.m
     n = s.min() if live_min else cal0.n
-    if p.reconstruction == mod.EXACT:
+    if p.reconstruction in (mod.EXACT, mod.EXP_BF16, mod.EXP_FP8):
         w = np.exp(s - m)
+        if p.reconstruction != mod.EXACT:
+            # straight-through rounding: the offset of the rounded exponential,
+            # frozen at s0, added before normalisation
+            e0 = np.exp(s0 - cal0.m)
+            w = w + (mod.round_to_format(e0, *mod.FORMATS[p.reconstruction]) - e0)
         rec = mod.reconstruct(s, m, 1.0, mod.Params(K=1))       # placeholder decisions (none)
         return float((w / w.sum()) @ dP), rec
     h = (m - n) / p.K if p.calibration == mod.MINMAX else p.tau / p.K
@@ -109,8 +114,14 @@ def torch_reexpression(mod, p, Q, Kt, V, dO):
             m = m.detach()
         if p.grad_rule in (mod.DETACH, mod.MAX_ONLY, mod.P1):
             n = n.detach()
-        if p.reconstruction == mod.EXACT:
+        if p.reconstruction in (mod.EXACT, mod.EXP_BF16, mod.EXP_FP8):
             w = torch.exp(s - m)
+            if p.reconstruction != mod.EXACT:
+                # torch's own casts round to nearest even (via fp32, whose extra
+                # rounding can matter only at an exact fp32 tie)
+                fmt = torch.bfloat16 if p.reconstruction == mod.EXP_BF16 else torch.float8_e4m3fn
+                wd = w.detach()
+                w = w + (wd.float().to(fmt).to(torch.float64) - wd)
             outs.append((w / w.sum()) @ v[: t + 1])
             continue
         if p.calibration == mod.MINMAX:

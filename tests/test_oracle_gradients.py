@@ -14,10 +14,11 @@ from tests.oracle_checks import (check_autograd, check_qkv_fd, check_score_fd,
 
 RULES = [O.FULL, O.DETACH, O.MAX_ONLY, O.MIN_ONLY]
 SURR = [(O.LERP, O.WEIGHT_STE), (O.NEAREST, O.WEIGHT_STE), (O.NEAREST, O.PROB_STE)]
+EXPS = [(O.EXACT, O.WEIGHT_STE), (O.EXP_BF16, O.WEIGHT_STE), (O.EXP_FP8, O.WEIGHT_STE)]
 
 
 @pytest.mark.parametrize("cal", [O.MINMAX, O.FWM, O.FWM_UNTRUNC])
-@pytest.mark.parametrize("rec,ste", SURR + [(O.EXACT, O.WEIGHT_STE)])
+@pytest.mark.parametrize("rec,ste", SURR + EXPS)
 @pytest.mark.parametrize("rule", RULES)
 @pytest.mark.parametrize("K", [1, 4, 16])
 def test_score_level_finite_differences(cal, rec, ste, rule, K):
@@ -37,7 +38,7 @@ def test_qkv_finite_differences_lerp_full(cal):
 
 
 @pytest.mark.parametrize("cal", [O.MINMAX, O.FWM, O.FWM_UNTRUNC])
-@pytest.mark.parametrize("rec,ste", SURR + [(O.EXACT, O.WEIGHT_STE)])
+@pytest.mark.parametrize("rec,ste", SURR + EXPS)
 @pytest.mark.parametrize("rule", RULES + [O.P1])
 def test_autograd_reexpression(cal, rec, ste, rule):
     rng = np.random.default_rng(31)
@@ -120,8 +121,17 @@ MUTANTS = [
      "i = np.maximum(np.floor(uc), 0).astype(np.int64)", "i = np.clip(np.floor(uc), 0, K - 1).astype(np.int64)",
      lambda m: check_autograd(m, m.Params(K=2, tau=1.0, calibration=m.FWM_UNTRUNC), *_head_inputs(T=12, d=6))),
     ("exact softmax gradient taken at the unnormalised weights",
-     "gt = (dP - delta) / fw.W\n        dS_direct = gt * fw.w", "gt = (dP - delta)\n        dS_direct = gt * fw.w",
+     "gt = (dP - delta) / fw.W\n        e = np.exp", "gt = (dP - delta)\n        e = np.exp",
      lambda m: check_autograd(m, m.Params(K=4, reconstruction=m.EXACT), *_head_inputs(T=12, d=6))),
+    ("straight-through derivative taken at the rounded exponentials",
+     "dS_direct = gt * e ", "dS_direct = gt * fw.w ",
+     lambda m: check_score_fd(m, m.Params(K=4, reconstruction=m.EXP_BF16), *_row_inputs())),
+    ("rounded exponential truncated instead of rounded to nearest",
+     "return np.rint(x / quantum) * quantum", "return np.floor(x / quantum) * quantum",
+     lambda m: check_autograd(m, m.Params(K=4, reconstruction=m.EXP_FP8), *_head_inputs(T=12, d=6))),
+    ("FP8 exponential without gradual underflow",
+     "FORMATS = {EXP_BF16: (7, -126), EXP_FP8: (3, -6)}", "FORMATS = {EXP_BF16: (7, -126), EXP_FP8: (3, -60)}",
+     lambda m: check_autograd(m, m.Params(K=4, reconstruction=m.EXP_FP8), *_head_inputs(T=12, d=6))),
     ("Nearest truncates instead of rounding (forward checked by autograd forward value)",
      "r = np.clip(np.floor(uc + 0.5), 0, K)", "r = np.clip(np.floor(uc), 0, K)",
      lambda m: check_autograd(m, m.Params(K=4, reconstruction=m.NEAREST), *_head_inputs(T=12, d=6))),

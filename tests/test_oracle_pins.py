@@ -397,3 +397,87 @@ def test_exact_reference_is_softmax(rule):
     np.testing.assert_allclose(fw.P, P, rtol=1e-13, atol=0)
     bw = O.row_backward(fw, dP, p)
     np.testing.assert_allclose(bw.dS, P * (dP - P @ dP), rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# reduced-precision exponential baselines (App. D.5; reading R14)
+# ---------------------------------------------------------------------------
+
+def _format_probe_values():
+    """fp32 values over the range the rounded exponentials take: random values
+    across the exponent range, their neighbours, and exact ties of both
+    formats (so round-half-even is exercised)."""
+    rng = np.random.default_rng(61)
+    x = np.exp(-rng.uniform(0, 40, 20000))
+    ties = []
+    for frac_bits, emin in ((7, -126), (3, -6)):
+        for E in range(-12, 0):
+            q = 2.0 ** (max(E, emin) - frac_bits)
+            for k in range(0, 2 ** (frac_bits + 1)):
+                v = 2.0 ** E + (k + 0.5) * q
+                if v < 2.0 ** (E + 1):
+                    ties.append(v)
+        for k in range(0, 16):                      # subnormal ties of E4M3
+            ties.append((k + 0.5) * 2.0 ** -9)
+    return np.concatenate([x, np.array(ties), [0.0, 1.0]]).astype(np.float32)
+
+
+@pytest.mark.parametrize("rec", [O.EXP_BF16, O.EXP_FP8])
+def test_rounding_matches_torch_casts(rec):
+    """round_to_format against torch's own round-to-nearest-even casts of
+    fp32 values to bfloat16 and float8_e4m3fn (library routines)."""
+    import torch
+    x = _format_probe_values()
+    fmt = torch.bfloat16 if rec == O.EXP_BF16 else torch.float8_e4m3fn
+    want = torch.from_numpy(x).to(fmt).to(torch.float64).numpy()
+    got = O.round_to_format(x.astype(np.float64), *O.FORMATS[rec])
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, [(float(x[i]), got[i], want[i]) for i in bad[:5]]
+
+
+@pytest.mark.parametrize("rec", [O.EXP_BF16, O.EXP_FP8])
+def test_rounded_exponential_on_representable_row_is_softmax(rec):
+    """Scores at m - j ln 2 have exponentials 2^-j, exact in both formats
+    (down to 2^-9 for E4M3), so the rounded baseline is softmax there."""
+    j = np.array([0, 1, 3, 2, 5, 9, 0, 4])
+    s = 1.5 - j * math.log(2.0)
+    p = Params(K=4, reconstruction=rec)
+    fw = O.row_forward(s, p)
+    np.testing.assert_array_equal(fw.w, 2.0 ** -j)
+    w = 2.0 ** -j
+    np.testing.assert_allclose(fw.P, w / w.sum(), rtol=1e-15, atol=0)
+
+
+def test_fp8_exponential_underflow_closed_form():
+    """E4M3 keeps nothing below half its smallest subnormal 2^-9: a key 8 nats
+    below the max (e^-8 < 2^-10) gets P = 0, yet straight-through still gives
+    it the direct term (dP - delta) e^-8 / W; a key ln 2 below gets 1/2."""
+    s = np.array([0.0, -8.0, -math.log(2.0)])
+    dP = np.array([0.3, -1.2, 0.7])
+    for rule in (O.FULL, O.DETACH):
+        p = Params(K=4, reconstruction=O.EXP_FP8, grad_rule=rule)
+        fw = O.row_forward(s, p)
+        np.testing.assert_array_equal(fw.w, [1.0, 0.0, 0.5])
+        W = 1.5
+        P = np.array([1.0, 0.0, 0.5]) / W
+        delta = P @ dP
+        bw = O.row_backward(fw, dP, p)
+        e = np.exp(s)
+        direct = (dP - delta) * e / W
+        want = direct.copy()
+        if rule == O.FULL:
+            want[0] = direct[0] - direct.sum()          # the max carries -sum(direct)
+        np.testing.assert_allclose(bw.dS, want, rtol=1e-14, atol=1e-16)
+
+
+@pytest.mark.parametrize("rec", [O.EXP_BF16, O.EXP_FP8])
+def test_rounded_exponential_zero_sum_under_full_only(rec):
+    rng = np.random.default_rng(62)
+    s = rng.standard_normal(30) * 3
+    dP = rng.standard_normal(30)
+    full = O.row_backward(O.row_forward(s, Params(K=4, reconstruction=rec)), dP, Params(K=4, reconstruction=rec))
+    assert abs(full.dS.sum()) <= 1e-14 * np.abs(full.dS).sum()
+    pd = Params(K=4, reconstruction=rec, grad_rule=O.DETACH)
+    det = O.row_backward(O.row_forward(s, pd), dP, pd)
+    # the rounding leaves sum_j P_j dP_j - delta * sum_j e_j / W != 0 under detach
+    assert abs(det.dS.sum()) > 1e-6 * np.abs(det.dS).sum()
