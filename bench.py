@@ -99,7 +99,8 @@ def _oracle_slice(args):
     wname, variant, b, h = args
     q, k, v, do = _cached_inputs(wname)
     cal = {"minmax": O.MINMAX, "fwm": O.FWM, "fwm_untrunc": O.FWM_UNTRUNC}[variant["calibration"]]
-    rec = {"lerp": O.LERP, "nearest": O.NEAREST, "exact": O.EXACT}[variant["reconstruction"]]
+    rec = {"lerp": O.LERP, "nearest": O.NEAREST, "exact": O.EXACT, "exp_bf16": O.EXP_BF16,
+           "exp_fp8": O.EXP_FP8}[variant["reconstruction"]]
     ste = {"weight": O.WEIGHT_STE, "prob": O.PROB_STE}[variant["surrogate"]]
     rule = {"full": O.FULL, "detach": O.DETACH, "max_only": O.MAX_ONLY, "min_only": O.MIN_ONLY,
             "p1": O.P1}[variant["grad_rule"]]
@@ -232,7 +233,7 @@ def main():
     ap.add_argument("--workload", default="c2", choices=sorted(DEFAULT_VARIANT))
     ap.add_argument("--K", type=int)
     ap.add_argument("--calibration", choices=["minmax", "fwm", "fwm_untrunc"])
-    ap.add_argument("--reconstruction", choices=["lerp", "nearest", "exact"])
+    ap.add_argument("--reconstruction", choices=["lerp", "nearest", "exact", "exp_bf16", "exp_fp8"])
     ap.add_argument("--surrogate", choices=["weight", "prob"])
     ap.add_argument("--grad-rule", dest="grad_rule", choices=["full", "detach", "max_only", "min_only", "p1"])
     ap.add_argument("--cpu-slices", type=int, default=96,

@@ -55,7 +55,7 @@ typedef enum kia_status {
 } kia_status;
 
 enum { KIA_CAL_MINMAX = 0, KIA_CAL_FWM = 1, KIA_CAL_FWM_UNTRUNC = 2 };
-enum { KIA_REC_LERP = 0, KIA_REC_NEAREST = 1, KIA_REC_EXACT = 2 };
+enum { KIA_REC_LERP = 0, KIA_REC_NEAREST = 1, KIA_REC_EXACT = 2, KIA_REC_EXP_BF16 = 3, KIA_REC_EXP_FP8 = 4 };
 /* KIA_CAL_FWM_UNTRUNC is the untruncated fixed-step operator of the paper's
  * tail-policy comparison (App. D.4): FWM's step h = tau/K anchored at the row
  * max, with the grid continued below max - tau instead of a zero tail (the
@@ -64,7 +64,14 @@ enum { KIA_REC_LERP = 0, KIA_REC_NEAREST = 1, KIA_REC_EXACT = 2 };
  * same path (App. D.5 compares against softmax): w = exp(s - max), with the
  * calibration, tau and surrogate flags ignored; its calibration term through
  * the max vanishes up to rounding, so every rule yields the softmax
- * gradient. */
+ * gradient.  KIA_REC_EXP_BF16 and KIA_REC_EXP_FP8 are the reduced-precision
+ * exponential baselines (App. D.5, Table S11): the exact reference with each
+ * exp(s - max) rounded to nearest (ties to even) in bf16, or in FP8 E4M3
+ * (3 fraction bits, subnormal step 2^-9; the pages name no FP8 format, E4M3
+ * is the forward-pass one), before normalisation.  Their backward is
+ * straight-through: the rounding counts as the identity, so the direct term
+ * uses the unrounded exponential with the Jacobian at the rounded P, and the
+ * max carries minus the row's direct sum under full and max-only. */
 enum { KIA_STE_WEIGHT = 0, KIA_STE_PROB = 1 };  /* read only for Nearest */
 enum { KIA_GRAD_FULL = 0, KIA_GRAD_DETACH = 1, KIA_GRAD_MAX_ONLY = 2, KIA_GRAD_MIN_ONLY = 3, KIA_GRAD_P1 = 4 };
 /* KIA_GRAD_P1 is the zero-sum projection of the detached gradient (App. B;
@@ -179,7 +186,8 @@ kia_status kia_backward_ext(const kia_params* p, int B, int H, int T, int d,
  *   SPAN      max - min of the row's scores
  *   WIDTH     the interval width h the operator lays on the row (MinMax
  *             span/K, 0 on rows below the degenerate span; FWM and
- *             FWM_UNTRUNC tau/K; under KIA_REC_EXACT the MinMax width span/K)
+ *             FWM_UNTRUNC tau/K; under KIA_REC_EXACT and the rounded
+ *             baselines the MinMax width span/K)
  *   Q_NORM    |Q_t|, K_NORM |K_t| (unscaled projections at position t)
  *   ENTROPY_P entropy (nats) of the operator's probabilities P
  *   ENTROPY_S entropy of the softmax of the same scores

@@ -18,7 +18,7 @@ from . import _lib
 from ._lib import KiaExt, KiaParams, KiaStatsLayout, KiaWorkspaceLayout
 
 CAL = {"minmax": 0, "fwm": 1, "fwm_untrunc": 2}
-REC = {"lerp": 0, "nearest": 1, "exact": 2}
+REC = {"lerp": 0, "nearest": 1, "exact": 2, "exp_bf16": 3, "exp_fp8": 4}
 STE = {"weight": 0, "prob": 1}
 RULE = {"full": 0, "detach": 1, "max_only": 2, "min_only": 3, "p1": 4}
 

@@ -20,10 +20,10 @@ kia_status check_params(const kia_params* p) {
     if (!p) return KIA_ERR_NULL;
     if (p->n_intervals < 1 || p->n_intervals > kMaxIntervals) return KIA_ERR_PARAM;
     if (p->calibration < KIA_CAL_MINMAX || p->calibration > KIA_CAL_FWM_UNTRUNC) return KIA_ERR_PARAM;
-    if (p->reconstruction < KIA_REC_LERP || p->reconstruction > KIA_REC_EXACT) return KIA_ERR_PARAM;
+    if (p->reconstruction < KIA_REC_LERP || p->reconstruction > KIA_REC_EXP_FP8) return KIA_ERR_PARAM;
     if (p->surrogate != KIA_STE_WEIGHT && p->surrogate != KIA_STE_PROB) return KIA_ERR_PARAM;
     if (p->grad_rule < KIA_GRAD_FULL || p->grad_rule > KIA_GRAD_P1) return KIA_ERR_PARAM;
-    if (p->calibration != KIA_CAL_MINMAX && p->reconstruction != KIA_REC_EXACT &&
+    if (p->calibration != KIA_CAL_MINMAX && p->reconstruction < KIA_REC_EXACT &&
         !(p->tau > 0.f && isfinite(p->tau)))
         return KIA_ERR_PARAM;
     return KIA_OK;
@@ -94,9 +94,10 @@ kia_status record(const kia_ext* ext, int i, hipStream_t st) {
     return hipEventRecord((hipEvent_t)ext->events[i], st) == hipSuccess ? KIA_OK : KIA_ERR_HIP;
 }
 
-// The exact-softmax reference is anchored at the row max only; it runs on the
-// FWM instantiation, whose grid constants it never reads.
-bool exact(const kia_params* p) { return p->reconstruction == KIA_REC_EXACT; }
+// The exact-softmax reference and its rounded baselines are anchored at the
+// row max only; they run on the FWM instantiation, whose grid constants they
+// never read.
+bool exact(const kia_params* p) { return p->reconstruction >= KIA_REC_EXACT; }
 float tau_of(const kia_params* p) { return exact(p) ? 1.f : p->tau; }
 
 kia::FwdConfig config_of(const kia_params* p, int d, bool dump) {

@@ -174,10 +174,15 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
                     const int key = k0 + acc_row(r, hl);
                     const bool valid = DIAG ? key <= qrow : true;
                     const float s = scur[r];
-                    if (REC == REC_EXACT) {
-                        // exact-softmax reference: P = exp(s - m) / W, direct term (dP - delta) P W / W_e
+                    if (softmax_rec(REC)) {
+                        // exact-softmax reference: P = exp(s - m) / W, direct term
+                        // (dP - delta) P W / W_e.  The rounded baselines keep that
+                        // direct term (straight-through) and store the rounded P.
                         const float pw = fast_exp2(fmaf(s - rg.m, kLog2e, lw));
-                        pr[r] = valid ? pw : 0.f;
+                        if (REC == REC_EXACT)
+                            pr[r] = valid ? pw : 0.f;
+                        else
+                            pr[r] = (valid && qvalid) ? round_exp<REC>(fast_exp2((s - rg.m) * kLog2e)) * invW : 0.f;
                         ds[r] = valid ? fmaf(dp[r], gW, ndW) * pw : 0.f;
                         SA += ds[r];
                         continue;
@@ -450,8 +455,12 @@ static hipError_t launch_rows_t(const BwdArgs& a, hipStream_t s) {
 
 template <int D, int CAL>
 static hipError_t launch_rows_rec(const FwdConfig& c, const BwdArgs& a, hipStream_t s) {
-    if (c.rec == REC_EXACT) {
-        if constexpr (CAL == CAL_FWM) return launch_rows_t<D, CAL, REC_EXACT, false>(a, s);
+    if (softmax_rec(c.rec)) {
+        if constexpr (CAL == CAL_FWM) {
+            if (c.rec == REC_EXACT) return launch_rows_t<D, CAL, REC_EXACT, false>(a, s);
+            if (c.rec == REC_EXP_BF16) return launch_rows_t<D, CAL, REC_EXP_BF16, false>(a, s);
+            return launch_rows_t<D, CAL, REC_EXP_FP8, false>(a, s);
+        }
         return hipErrorInvalidValue;
     }
     if (c.rec == REC_LERP) return launch_rows_t<D, CAL, REC_LERP, false>(a, s);

@@ -26,7 +26,10 @@ constexpr int kTileElems = kTile * kTile;
 constexpr int kWave = 64;
 
 enum { CAL_MINMAX = 0, CAL_FWM = 1, CAL_FWM_UNTRUNC = 2 };
-enum { REC_LERP = 0, REC_NEAREST = 1, REC_EXACT = 2 };
+enum { REC_LERP = 0, REC_NEAREST = 1, REC_EXACT = 2, REC_EXP_BF16 = 3, REC_EXP_FP8 = 4 };
+// Softmax anchored at the row max, no grid: the exact reference and its
+// rounded-exponential baselines.
+constexpr bool softmax_rec(int rec) { return rec >= REC_EXACT; }
 
 enum { GRAD_FULL = 0, GRAD_DETACH = 1, GRAD_MAX_ONLY = 2, GRAD_MIN_ONLY = 3, GRAD_P1 = 4 };
 
@@ -345,6 +348,26 @@ __device__ __forceinline__ RowGrid make_row_grid(float m, float n, int K, float 
 // may flush to zero; that changes a normalised probability by less than
 // 1e-38 relative.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Rounded exponentials of the reduced-precision baselines (App. D.5): a
+// non-negative fp32 value (at most 1 here) rounded to nearest, ties to even,
+// in bf16 (7 fraction bits) or FP8 E4M3 (3 fraction bits, smallest normal
+// 2^-6, subnormal step 2^-9), returned as the fp32 value it represents.
+template <int REC>
+__device__ __forceinline__ float round_exp(float e) {
+    if constexpr (REC == REC_EXP_BF16) {
+        uint32_t b = __float_as_uint(e);
+        b += 0x7fffu + ((b >> 16) & 1u);
+        return __uint_as_float(b & 0xffff0000u);
+    } else if constexpr (REC == REC_EXP_FP8) {
+        if (e < 0.015625f) return rintf(e * 512.f) * 0.001953125f;  // multiples of 2^-9
+        uint32_t b = __float_as_uint(e);
+        b += 0x7ffffu + ((b >> 20) & 1u);
+        return __uint_as_float(b & 0xfff00000u);
+    } else {
+        return e;
+    }
+}
 
 // Reconstruction of one score.  u = (m - s)/h >= 0 (distance below the row
 // max in grid steps); LERP segment i = min(floor(u), K-1), f = u - i, weight

@@ -226,9 +226,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
         const int key = kt_t * kTile + acc_row(r, hl);
         const bool valid = DIAG ? key <= qrow : true;
         const float s = sv[r];
-        if (REC == REC_EXACT) {
-            // exact-softmax reference: w = exp(s - m)
-            w[r] = valid ? fast_exp2((s - rg.m) * kLog2e) : 0.f;
+        if (softmax_rec(REC)) {
+            // exact-softmax reference w = exp(s - m), or its rounded baselines
+            w[r] = valid ? round_exp<REC>(fast_exp2((s - rg.m) * kLog2e)) : 0.f;
             Wt += w[r];
             if (DUMP && qvalid && valid) a.idx_dump[((size_t)bh * T + qrow) * T + key] = 0;
             return;
@@ -372,11 +372,18 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
 
 template <int D, int CAL>
 static hipError_t launch_fwd_rec(const FwdConfig& c, const FwdArgs& a, hipStream_t s) {
-    if (c.rec == REC_EXACT) {
-        // the exact reference is anchored at the max only: built on the FWM path
-        if constexpr (CAL == CAL_FWM)
-            return c.dump ? launch_fwd_t<D, CAL, REC_EXACT, false, true>(a, s)
-                          : launch_fwd_t<D, CAL, REC_EXACT, false, false>(a, s);
+    if (softmax_rec(c.rec)) {
+        // softmax anchored at the max only: built on the FWM path
+        if constexpr (CAL == CAL_FWM) {
+            if (c.rec == REC_EXACT)
+                return c.dump ? launch_fwd_t<D, CAL, REC_EXACT, false, true>(a, s)
+                              : launch_fwd_t<D, CAL, REC_EXACT, false, false>(a, s);
+            if (c.rec == REC_EXP_BF16)
+                return c.dump ? launch_fwd_t<D, CAL, REC_EXP_BF16, false, true>(a, s)
+                              : launch_fwd_t<D, CAL, REC_EXP_BF16, false, false>(a, s);
+            return c.dump ? launch_fwd_t<D, CAL, REC_EXP_FP8, false, true>(a, s)
+                          : launch_fwd_t<D, CAL, REC_EXP_FP8, false, false>(a, s);
+        }
         return hipErrorInvalidValue;
     }
     if (c.rec == REC_LERP)

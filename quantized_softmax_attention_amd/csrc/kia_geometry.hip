@@ -6,8 +6,8 @@
 //
 // Fields, each an fp32 array over the B*H*T rows: span (max - min), native
 // width h (the operator's interval width: MinMax span/K, 0 on degenerate
-// rows; FWM and the untruncated step tau/K; the exact reference reports the
-// MinMax width), |Q_t|, |K_t|, entropy of P, entropy of the softmax (nats),
+// rows; FWM and the untruncated step tau/K; the exact reference and its
+// rounded-exponential baselines report the MinMax width), |Q_t|, |K_t|, entropy of P, entropy of the softmax (nats),
 // total variation (1/2) sum |P - softmax|, and the softmax mass of the top
 // rounding bucket (keys whose Nearest point on that grid is 0).
 #include <type_traits>
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kGeoWaves * kWave) void kia_geometry_kernel(GeoArgs
 
     // the operator's grid; the exact reference lays a MinMax grid for the
     // reported width and the top bucket
-    constexpr int GCAL = (REC == REC_EXACT) ? CAL_MINMAX : CAL;
+    constexpr int GCAL = softmax_rec(REC) ? CAL_MINMAX : CAL;
     const RowGrid rg = make_row_grid(m, mn, a.K, a.tau, GCAL == CAL_MINMAX ? CAL_MINMAX : CAL_FWM);
     const float W = qvalid ? a.row_w[row] : 1.f;
     const float invW = 1.f / W;
@@ -128,6 +128,9 @@ __global__ __launch_bounds__(kGeoWaves * kWave) void kia_geometry_kernel(GeoArgs
                 if (REC == REC_EXACT) {
                     w = e;
                     lw = xe * kLn2;
+                } else if (softmax_rec(REC)) {
+                    w = round_exp<REC>(e);
+                    lw = __logf(w);
                 } else if (REC == REC_NEAREST) {
                     const float xr = -floorf(u + 0.5f) * rg.hl2;
                     const bool keep = (CAL == CAL_FWM) ? (u <= rg.Kf) : true;
@@ -234,6 +237,8 @@ hipError_t launch_geo_rec(int rec, const GeoArgs& a, hipStream_t s) {
 hipError_t launch_geometry(int cal, int rec, const GeoArgs& a, hipStream_t s) {
     static_assert(kGeoFields == 8, "field count");
     if (rec == REC_EXACT) return launch_geo_t<CAL_MINMAX, REC_EXACT>(a, s);
+    if (rec == REC_EXP_BF16) return launch_geo_t<CAL_MINMAX, REC_EXP_BF16>(a, s);
+    if (rec == REC_EXP_FP8) return launch_geo_t<CAL_MINMAX, REC_EXP_FP8>(a, s);
     if (cal == CAL_MINMAX) return launch_geo_rec<CAL_MINMAX>(rec, a, s);
     if (cal == CAL_FWM) return launch_geo_rec<CAL_FWM>(rec, a, s);
     return launch_geo_rec<CAL_FWM_UNTRUNC>(rec, a, s);

@@ -29,7 +29,8 @@ ZERO_SUM_TOL = 1e-5
 
 def to_oracle_params(p):
     cal = {"minmax": O.MINMAX, "fwm": O.FWM, "fwm_untrunc": O.FWM_UNTRUNC}[p.calibration]
-    rec = {"lerp": O.LERP, "nearest": O.NEAREST, "exact": O.EXACT}[p.reconstruction]
+    rec = {"lerp": O.LERP, "nearest": O.NEAREST, "exact": O.EXACT, "exp_bf16": O.EXP_BF16,
+           "exp_fp8": O.EXP_FP8}[p.reconstruction]
     ste = {"weight": O.WEIGHT_STE, "prob": O.PROB_STE}[p.surrogate]
     rule = {"full": O.FULL, "detach": O.DETACH, "max_only": O.MAX_ONLY, "min_only": O.MIN_ONLY,
             "p1": O.P1}[p.grad_rule]
@@ -179,17 +180,20 @@ class SliceCheck:
             if t >= 1:
                 if srt[-1] - srt[-2] <= tie_band:
                     ab_amb = True
-                if p.calibration == O.MINMAX and p.reconstruction != O.EXACT and srt[1] - srt[0] <= tie_band:
+                if p.calibration == O.MINMAX and p.reconstruction not in O.EXP_FAMILY \
+                        and srt[1] - srt[0] <= tie_band:
                     ab_amb = True
             if not ab_amb:
                 assert g["a"][t] == cal.a, ("argmax", t, g["a"][t], cal.a)
-                if p.calibration == O.MINMAX and p.reconstruction != O.EXACT:
+                if p.calibration == O.MINMAX and p.reconstruction not in O.EXP_FAMILY:
                     assert g["b"][t] == cal.b, ("argmin", t, g["b"][t], cal.b)
-            if cal.degenerate or t == 0 or p.reconstruction == O.EXACT:
+            if cal.degenerate or t == 0 or p.reconstruction in O.EXP_FAMILY:
                 if ab_amb:
                     self.amb_bwd[t] = True
-                    if p.reconstruction == O.EXACT:
+                    if p.reconstruction in O.EXP_FAMILY:
                         self.amb_keys_bwd.update(range(t + 1))
+                if p.reconstruction in O.FORMATS and t > 0 and sg is not None:
+                    self._rounding_band(t, fw, sg)
                 continue
             # decision band in grid steps
             mg, ng = float(g["m"][t]), float(g["n"][t])
@@ -246,6 +250,33 @@ class SliceCheck:
                 ok = ~amb
                 self.idx_checked += int(ok.sum())
                 self.idx_mismatch += int((gi[ok] != ri[ok]).sum())
+
+    def _rounding_band(self, t, fw, sg):
+        """Rounded-exponential baselines: a key whose exp(s - m) lies closer to
+        a rounding midpoint of the format than the two sides' exponentials can
+        differ may round either way.  The kernel's exponential carries the
+        difference of its fp32 s - m from the oracle's, plus the rounding of
+        the argument and of its exp2 (a few 2^-24 relative each)."""
+        frac_bits, emin = O.FORMATS[self.p.reconstruction]
+        m_ref = fw.cal.m
+        x_ref = fw.s - m_ref
+        e_ref = np.exp(x_ref)
+        d_obs = np.abs((sg - float(self.g["m"][t])) - x_ref)
+        band = 2 * e_ref * (d_obs + 8 * 2.0 ** -24 * (np.abs(x_ref) + 1))
+        _, ex = np.frexp(e_ref)
+        q = np.ldexp(1.0, np.maximum(ex - 1, emin) - frac_bits)
+        dist = np.abs(e_ref / q - np.floor(e_ref / q) - 0.5) * q
+        amb = dist <= band
+        if not amb.any():
+            return
+        self.n_amb_pairs += int(amb.sum())
+        rel = float(q[amb].max()) / fw.W          # one quantum against the row normaliser
+        if rel > 1e-7:
+            self.amb_fwd[t] = True
+            self.fwd_unstable_rows.append((t, rel))
+        self.amb_bwd[t] = True
+        self.amb_keys_bwd.update(int(j) for j in np.flatnonzero(amb))
+        self.amb_keys_bwd.add(int(fw.cal.a))
 
     # ------------------------------------------------------------------
     def compare(self, name, tol=TOL):

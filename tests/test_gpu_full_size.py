@@ -44,7 +44,7 @@ def zero_sum_all_rows(g, params, tol=1e-5):
     sums = dS.double().sum(-1)
     l1 = dS.double().abs().sum(-1)
     bad = sums.abs() > tol * l1
-    if params.calibration == "minmax" and params.reconstruction != "exact":
+    if params.calibration == "minmax" and params.reconstruction not in ("exact", "exp_bf16", "exp_fp8"):
         bad &= (g["m"] - g["n"]).double() >= 1e-12
     idx = torch.nonzero(bad)[:5].tolist()
     detail = [(tuple(i), float(sums[tuple(i)]), float(l1[tuple(i)]), int(g["a"][tuple(i)]), int(g["b"][tuple(i)]),
@@ -115,6 +115,16 @@ def test_c2_full_size_exact_softmax(rule):
     makes each row sum exact; under detach the direct terms cancel only to the
     rounding of delta = dO.O, so the row-sum bar applies to the full rule."""
     full_check("c2", P(K=1, reconstruction="exact", grad_rule=rule), _heads(30, WORKLOADS["c2"]),
+               zero_sum=(rule == "full"))
+
+
+@pytest.mark.parametrize("rec", ["exp_bf16", "exp_fp8"])
+@pytest.mark.parametrize("rule", ["full", "detach"])
+def test_c2_full_size_rounded_exponential(rec, rule):
+    """The BF16- and FP8-rounded exponential baselines at full size; the row
+    sum vanishes under the full rule only."""
+    full_check("c2", P(K=1, reconstruction=rec, grad_rule=rule), _heads(31 if rec == "exp_bf16" else 32,
+                                                                       WORKLOADS["c2"]),
                zero_sum=(rule == "full"))
 
 

@@ -56,7 +56,8 @@ COMBOS = [("minmax", "lerp", "weight"), ("fwm", "lerp", "weight"),
           ("minmax", "nearest", "weight"), ("minmax", "nearest", "prob"),
           ("fwm", "nearest", "weight"), ("fwm", "nearest", "prob"),
           ("fwm_untrunc", "lerp", "weight"), ("fwm_untrunc", "nearest", "weight"),
-          ("fwm_untrunc", "nearest", "prob"), ("minmax", "exact", "weight")]
+          ("fwm_untrunc", "nearest", "prob"), ("minmax", "exact", "weight"),
+          ("minmax", "exp_bf16", "weight"), ("minmax", "exp_fp8", "weight")]
 RULES = ["full", "detach", "max_only", "min_only", "p1"]
 
 

@@ -101,7 +101,8 @@ def _bwd(lib, p, ptrs=None, nbytes=1 << 40, wbytes=1 << 40, T=8, d=64):
 
 
 @pytest.mark.parametrize("field,value", [("n_intervals", 0), ("n_intervals", 65537), ("calibration", 3),
-                                         ("reconstruction", -1), ("surrogate", 3), ("grad_rule", 5)])
+                                         ("reconstruction", -1), ("reconstruction", 5), ("surrogate", 3),
+                                         ("grad_rule", 5)])
 def test_bad_params_rejected(field, value):
     lib, mod = _lib()
     p = _params(mod)
