@@ -172,7 +172,7 @@ def _counter_means(d, counter):
 
 def _kernel_key(name):
     for key, pat in (("forward", "kia_forward_kernel"), ("backward_rows", "kia_backward_rows_kernel"),
-                     ("backward_cols", "kia_backward_cols_kernel")):
+                     ("backward_cols", "kia_backward_cols_kernel"), ("geometry", "kia_geometry_kernel")):
         if pat in name:
             return key
     return None
@@ -355,16 +355,24 @@ def main():
                  "bytes_per_launch": probe_bytes, "achieved": round(gbps, 1), "peak": PEAK_HBM,
                  "unit": "GB/s", "frac": round(gbps / PEAK_HBM, 4)}
 
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
+    def measured_traffic(kernel):
+        """HBM bytes per launch from the committed counter run, while the
+        kernel sources, workload and variant still match it; else None."""
+        if not os.path.exists(TRAFFIC_FILE):
+            return None
         try:
             tr = json.load(open(TRAFFIC_FILE))
-            ent = tr.get("kernels", {}).get(dominant)
+            ent = tr.get("kernels", {}).get(kernel)
             if ent and tr.get("source_digest") == source_digest() and tr.get("workload") == args.workload \
                     and tr.get("variant") == variant:
-                traffic = ent["hbm_bytes_per_launch"]
+                return ent["hbm_bytes_per_launch"]
         except (ValueError, KeyError):
-            traffic = None
+            return None
+        return None
+
+    traffic = measured_traffic(dominant)
+    if probe is not None:
+        probe["traffic"] = measured_traffic("geometry")
 
     value = flop_step / (ms_step * 1e-3) / 1e12
     out = {
