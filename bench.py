@@ -59,12 +59,18 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
+# timing-only events: no system-scope fence (cache writeback and invalidate)
+# when they are recorded, so recording one around every kernel of every timed
+# step leaves the kernels' own behaviour unchanged
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
 class HipEvents:
     """Raw hipEvent_t handles (the library records them on the launch stream)."""
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.events = []
@@ -73,8 +79,8 @@ class HipEvents:
         out = []
         for _ in range(n):
             e = ctypes.c_void_p()
-            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
             out.append(e.value)
         self.events.extend(out)
         return out
