@@ -1,0 +1,104 @@
+"""The library on a caller's stream and under HIP graph capture.
+
+The C ABI launches only on the stream it is given, never allocates and never
+synchronises, so a forward + backward can run on any stream and be captured
+into a graph.  Results are deterministic (no atomics), so every check here is
+bitwise: a side stream against the current stream, and every replay of a
+captured step against the eager step on the same inputs.  Between replays
+the test runs other eager work (a step on different inputs) and synchronises,
+and it checks each replay, not only the last.
+"""
+import numpy as np
+import pytest
+
+from workloads import Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+W = Workload("streams", 2, 3, 200, 64, "scaled", q_scale=2.0)
+
+
+def _params(**kw):
+    from quantized_softmax_attention_amd import Params
+    return Params(**kw)
+
+
+def _tensors(seed_shift=0):
+    import torch
+    q, k, v, do = make_inputs(W)
+    if seed_shift:
+        q = np.roll(q, seed_shift, axis=2)
+    dev = torch.device("cuda:0")
+    return tuple(torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (q, k, v, do))
+
+
+def _step(kia, x, p, out, stream=None):
+    q, k, v, do = x
+    o, st, dq, dk, dv, ws = out
+    kia.kia_forward(q, k, v, p, o=o, stats=st, stream=stream)
+    kia.kia_backward(q, k, v, o, do, st, p, dq=dq, dk=dk, dv=dv, ws=ws, stream=stream)
+
+
+def _alloc(kia, x, p):
+    import torch
+    q = x[0]
+    B, H, T, d = q.shape
+    st = torch.empty(kia.kia_stats_bytes(p, B, H, T, d), dtype=torch.uint8, device=q.device)
+    ws = torch.empty(kia.kia_workspace_bytes(p, B, H, T, d), dtype=torch.uint8, device=q.device)
+    return (torch.empty_like(q), st, torch.empty_like(q), torch.empty_like(q), torch.empty_like(q), ws)
+
+
+VARIANTS = [dict(K=32), dict(K=4, calibration="fwm", reconstruction="nearest", surrogate="prob"),
+            dict(K=4, grad_rule="p1"), dict(K=1, reconstruction="exp_fp8")]
+
+
+@pytest.mark.parametrize("kw", VARIANTS, ids=lambda kw: "-".join(f"{k}={v}" for k, v in kw.items()))
+def test_side_stream_matches_current_stream(kw):
+    import torch
+    import quantized_softmax_attention_amd as kia
+    p = _params(**kw)
+    x = _tensors()
+    a, b = _alloc(kia, x, p), _alloc(kia, x, p)
+    print(f"[case] side stream {p}", flush=True)
+    _step(kia, x, p, a)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    _step(kia, x, p, b, stream=s)
+    torch.cuda.synchronize()
+    for name, ga, gb in zip(("o", "dq", "dk", "dv"), (a[0], a[2], a[3], a[4]), (b[0], b[2], b[3], b[4])):
+        assert torch.equal(ga, gb), name
+
+
+@pytest.mark.parametrize("kw", VARIANTS, ids=lambda kw: "-".join(f"{k}={v}" for k, v in kw.items()))
+def test_graph_replays_match_eager(kw):
+    import torch
+    import quantized_softmax_attention_amd as kia
+    p = _params(**kw)
+    x = _tensors()
+    other = _tensors(seed_shift=17)
+    eager = _alloc(kia, x, p)
+    print(f"[case] graph capture {p}", flush=True)
+    _step(kia, x, p, eager)
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (eager[0], eager[2], eager[3], eager[4])]
+
+    cap = _alloc(kia, x, p)
+    side = _alloc(kia, other, p)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        _step(kia, x, p, cap)             # warm the stream before capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            _step(kia, x, p, cap)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (cap[0], cap[2], cap[3], cap[4]):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        _step(kia, other, p, side)        # other eager work between replays
+        torch.cuda.synchronize()
+        for name, got, ref in zip(("o", "dq", "dk", "dv"), (cap[0], cap[2], cap[3], cap[4]), want):
+            assert torch.equal(got, ref), (rep, name)
