@@ -155,9 +155,11 @@ kia_status kia_backward(const kia_params* p, int B, int H, int T, int d,
 /* Optional extras for the two calls above.  events: NULL or an array of
  * hipEvent_t (as void*) recorded on `stream` around each kernel: forward
  * uses 2 (start/end of its one kernel), backward 4 (around its two kernels,
- * in launch order).  idx_dump (forward only): NULL or int32 [B,H,T,T]; for
- * every causal pair the kernel writes the grid index it used (the LERP
- * segment, or the Nearest grid point), -1 for keys outside the FWM window;
+ * in launch order; under KIA_GRAD_P1 the first interval also covers the
+ * key prefix-sum and row-centring launches).  idx_dump (forward only): NULL
+ * or int32 [B,H,T,T]; for every causal pair the kernel writes the grid index
+ * it used (the LERP segment, or the Nearest grid point), -1 for keys outside
+ * the FWM window, 0 under KIA_REC_EXACT and the rounded baselines (no grid);
  * non-causal entries are left untouched. */
 typedef struct kia_ext {
     void* const* events;
