@@ -89,3 +89,28 @@ def test_c1_single_head_full_and_detach():
     w = WORKLOADS["c1"]
     for rule in ("full", "detach"):
         check(w, P(K=32, calibration="minmax", reconstruction="lerp", grad_rule=rule))
+
+
+@pytest.mark.parametrize("cal", ["minmax", "fwm"])
+def test_small_largest_interval_count(cal):
+    """K = 65536, the largest the ABI accepts: h is ~2e-4 nats, so LERP is
+    close to softmax and u spans tens of thousands of grid steps.  The two
+    sides' u then differ by ~0.01 steps, so a few per cent of keys sit near a
+    knot; for LERP such a key moves only the derivative, by a relative ~h,
+    and is excluded from dK alone."""
+    check(SMALL, P(K=65536, tau=6.0, calibration=cal), max_amb_frac=0.1)
+
+
+@pytest.mark.parametrize("tau", [0.25, 60.0])
+@pytest.mark.parametrize("rec,ste", [("lerp", "weight"), ("nearest", "prob")])
+def test_small_fwm_window_extremes(tau, rec, ste):
+    """A window so narrow that most keys get zero weight, and one wider than
+    every row's span (FWM then never zeroes a key)."""
+    check(SMALL, P(K=4, tau=tau, calibration="fwm", reconstruction=rec, surrogate=ste))
+
+
+@pytest.mark.parametrize("rec", ["lerp", "nearest"])
+def test_small_untruncated_narrow_step(rec):
+    """The untruncated step with tau = 0.5, K = 2: the grid runs tens of
+    intervals below the window, far past the K of the truncated operator."""
+    check(SMALL, P(K=2, tau=0.5, calibration="fwm_untrunc", reconstruction=rec))
