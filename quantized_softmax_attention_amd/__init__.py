@@ -6,6 +6,7 @@ runs in the library's HIP kernels.  The functions keep the C names:
 
     o, stats = kia_forward(q, k, v, params)
     dq, dk, dv, ws = kia_backward(q, k, v, o, do, stats, params)
+    o = kia_attention(q, k, v, params)          # the same two calls as an autograd op
 
 with q, k, v, o, do fp32 CUDA tensors of shape [B, H, T, d], d in {64, 128}.
 """
@@ -202,10 +203,53 @@ def kia_tiles_to_dense(B, H, T, tiles, key_major: bool, dense=None, stream=None)
     return dense
 
 
+def kia_attention(q, k, v, params: Params):
+    """O = K-interval attention of q, k, v as a differentiable torch op: the
+    forward calls kia_forward, the backward kia_backward with the saved
+    stats (so dQ, dK, dV follow params' gradient rule and surrogate).  The
+    incoming gradient is made contiguous; no other work happens here."""
+    return _KiaAttention.apply(q, k, v, params)
+
+
+def _make_function():
+    torch = _torch()
+
+    class KiaAttention(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, params):
+            o, stats = kia_forward(q, k, v, params)
+            ctx.save_for_backward(q, k, v, o, stats)
+            ctx.params = params
+            return o
+
+        @staticmethod
+        def backward(ctx, do):
+            q, k, v, o, stats = ctx.saved_tensors
+            dq, dk, dv, _ = kia_backward(q, k, v, o, do.contiguous(), stats, ctx.params)
+            return dq, dk, dv, None
+
+    return KiaAttention
+
+
+class _Lazy:
+    """The autograd Function class, built on first use (torch is imported
+    only then)."""
+    fn = None
+
+    @classmethod
+    def apply(cls, *args):
+        if cls.fn is None:
+            cls.fn = _make_function()
+        return cls.fn.apply(*args)
+
+
+_KiaAttention = _Lazy
+
+
 def kia_abi_version() -> int:
     return int(_lib.load().kia_abi_version())
 
 
 __all__ = ["Params", "KiaError", "kia_forward", "kia_backward", "kia_stats_bytes",
            "kia_workspace_bytes", "kia_stats_layout_query", "kia_workspace_layout_query",
-           "kia_geometry", "GEOMETRY_FIELDS", "kia_tiles_to_dense", "kia_abi_version"]
+           "kia_geometry", "GEOMETRY_FIELDS", "kia_tiles_to_dense", "kia_abi_version", "kia_attention"]

@@ -1,4 +1,5 @@
-"""The library on a caller's stream and under HIP graph capture.
+"""The library on a caller's stream, under HIP graph capture, and through
+the autograd wrapper kia_attention.
 
 The C ABI launches only on the stream it is given, never allocates and never
 synchronises, so a forward + backward can run on any stream and be captured
@@ -102,3 +103,23 @@ def test_graph_replays_match_eager(kw):
         torch.cuda.synchronize()
         for name, got, ref in zip(("o", "dq", "dk", "dv"), (cap[0], cap[2], cap[3], cap[4]), want):
             assert torch.equal(got, ref), (rep, name)
+
+
+@pytest.mark.parametrize("kw", VARIANTS, ids=lambda kw: "-".join(f"{k}={v}" for k, v in kw.items()))
+def test_autograd_op_matches_direct_calls(kw):
+    """kia_attention (the autograd wrapper) returns kia_forward's O and, from
+    torch.autograd, exactly kia_backward's dQ, dK, dV."""
+    import torch
+    import quantized_softmax_attention_amd as kia
+    p = _params(**kw)
+    q, k, v, do = _tensors()
+    print(f"[case] autograd op {p}", flush=True)
+    o_ref, st = kia.kia_forward(q, k, v, p)
+    dq_ref, dk_ref, dv_ref, _ = kia.kia_backward(q, k, v, o_ref, do, st, p)
+    qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
+    o = kia.kia_attention(qa, ka, va, p)
+    dq, dk, dv = torch.autograd.grad(o, (qa, ka, va), grad_outputs=do)
+    torch.cuda.synchronize()
+    assert torch.equal(o.detach(), o_ref)
+    for name, got, ref in (("dq", dq, dq_ref), ("dk", dk, dk_ref), ("dv", dv, dv_ref)):
+        assert torch.equal(got, ref), name
