@@ -219,7 +219,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
             if (kt == qt) grads(std::true_type{});
             else grads(std::false_type{});
 
-            // P and dS to key-major tiles through the wave's LDS scratch
+            // P and dS to key-major tiles through the wave's LDS scratch; the
+            // column kernel reads them once, so the stores are non-temporal
             float* pp = ptiles + (size_t)kt * kTileElems;
             float* dd = dstiles + (size_t)kt * kTileElems;
 #pragma unroll
@@ -227,14 +228,14 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int p = 0; p < 4; ++p)
-                *(f32x4*)(pp + p * 256 + lane * 4) = *(const f32x4*)(xw + li * XS + 8 * p + 4 * hl);
+                __builtin_nontemporal_store(*(const f32x4*)(xw + li * XS + 8 * p + 4 * hl), (f32x4*)(pp + p * 256 + lane * 4));
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int r = 0; r < 16; ++r) xw[acc_row(r, hl) * XS + li] = ds[r];
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
             for (int p = 0; p < 4; ++p)
-                *(f32x4*)(dd + p * 256 + lane * 4) = *(const f32x4*)(xw + li * XS + 8 * p + 4 * hl);
+                __builtin_nontemporal_store(*(const f32x4*)(xw + li * XS + 8 * p + 4 * hl), (f32x4*)(dd + p * 256 + lane * 4));
             __builtin_amdgcn_wave_barrier();
 
             // dQ^T += K^T dS^T : A operand row = head-dim index

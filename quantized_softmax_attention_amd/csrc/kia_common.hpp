@@ -196,11 +196,15 @@ struct LdsTile {
 // score, probability and score-gradient tiles): lane l fetches its float4 of
 // each 1 KB chunk, which lands at the same place in the wave's LDS slot, so
 // the lane later reads back exactly the registers it would have loaded.
+// Each such tile is read once per kernel, so the loads are non-temporal
+// (cache policy NT): they do not displace the K, V, Q, dO tiles that every
+// workgroup of a slice re-reads from L2.
+constexpr int kCpolNonTemporal = 2;
 __device__ __forceinline__ void dma_tile(float* lds_wave, const float* src, int lane) {
 #pragma unroll
     for (int p = 0; p < 4; ++p)
         __builtin_amdgcn_global_load_lds((const void*)(src + p * 256 + lane * 4), lds_dst(lds_wave + p * 256), 16,
-                                         0, 0);
+                                         0, kCpolNonTemporal);
 }
 __device__ __forceinline__ void read_tile(const float* lds_wave, int lane, float* out) {
 #pragma unroll
