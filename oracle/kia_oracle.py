@@ -29,7 +29,7 @@ Attention" (paperlayer digest of the paper):
   surrogate; Weight-STE evaluates the normalisation Jacobian at the hard
   weights, Prob-STE at the LERP probabilities and normaliser.
 
-Readings where the pages leave a step open (each is listed in the design doc):
+Readings where the pages leave a step open:
   R1  Nearest rounds to the nearest grid point j*h (K+1 levels); a score
       exactly half-way rounds up in u, i.e. r = floor(u + 1/2).
   R2  LERP uses segment i = min(floor(u), K-1): at a knot the right-hand
