@@ -1,8 +1,8 @@
 """fp64 CPU oracle for K-interval attention.
 
-TEST INFRASTRUCTURE ONLY: imported by the test suite, the graft smoke check
-and the benchmark's CPU-baseline leg, never by the HIP library or its
-binding.  It shares no code with them.
+TEST INFRASTRUCTURE ONLY: imported by the test suite, smoke() in
+__graft_entry__.py and the benchmark's CPU-baseline leg, never by the HIP
+library or its binding.  It shares no code with them.
 """
 from .kia_oracle import (  # noqa: F401
     DETACH, EPS_SPAN, EXACT, EXP_BF16, EXP_FAMILY, EXP_FP8, FORMATS, FULL, FWM, FWM_UNTRUNC,

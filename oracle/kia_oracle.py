@@ -1,8 +1,7 @@
 """K-interval attention: plain fp64 CPU oracle.
 
-TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check of the graft
-entry module and the benchmark's CPU-baseline leg may import or run this
-file.  It shares no code, constant table or helper with the HIP library, and
+TEST INFRASTRUCTURE ONLY.  Only the test suite, smoke() in __graft_entry__.py
+and the benchmark's CPU-baseline leg may import or run this file.  It shares no code, constant table or helper with the HIP library, and
 the library never calls it.
 
 What it computes follows "Pretraining Transformers with Quantized Softmax in
