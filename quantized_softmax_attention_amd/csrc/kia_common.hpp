@@ -373,32 +373,4 @@ __device__ __forceinline__ float round_exp(float e) {
     }
 }
 
-// Reconstruction of one score.  u = (m - s)/h >= 0 (distance below the row
-// max in grid steps); LERP segment i = min(floor(u), K-1), f = u - i, weight
-// g_i (1 - f c) where g_i = exp(-i h) is grid value i; Nearest grid point
-// r = floor(u + 1/2), weight g_r.  Under MinMax u <= K up to one rounding
-// (the row min), which segment K-1 absorbs; under FWM keys with u > K are
-// outside the window (`inwin`) and get weight 0.
-struct Recon {
-    float u, fi, f, g, wl, wn;
-    bool inwin;
-};
-
-template <int CAL, bool NEED_NEAREST>
-__device__ __forceinline__ Recon reconstruct(const RowGrid& rg, float s) {
-    Recon e;
-    e.u = (rg.m - s) * rg.invh;
-    e.inwin = (CAL == CAL_FWM) ? (e.u <= rg.Kf) : true;
-    e.fi = fminf(floorf(e.u), rg.Kf - 1.f);
-    e.f = e.u - e.fi;
-    e.g = fast_exp2(-e.fi * rg.hl2);
-    e.wl = e.g * fmaf(-e.f, rg.c, 1.f);
-    if (NEED_NEAREST) {
-        e.wn = fast_exp2(-floorf(e.u + 0.5f) * rg.hl2);
-    } else {
-        e.wn = 0.f;
-    }
-    return e;
-}
-
 }  // namespace kia
