@@ -60,17 +60,42 @@ def _shape(q):
     return tuple(int(x) for x in q.shape)
 
 
-def _check(t, name, shape=None):
+def _check(t, name, shape=None, device=None):
+    """A contiguous fp32 GPU tensor (of the given shape, on the given device)."""
     torch = _torch()
-    if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous float32 GPU tensor")
     if shape is not None and tuple(t.shape) != shape:
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
-def _stream(stream):
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _buffer(t, name, nbytes, device):
+    """A contiguous GPU buffer of any dtype holding at least nbytes bytes."""
     torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if _nbytes(t) < nbytes:
+        raise ValueError(f"{name} holds {_nbytes(t)} bytes, the call needs {nbytes}")
+
+
+def _size_error(lib, query, cp, B, H, T, d, layout):
+    """The status of the size query's checks (a size query returns 0 on error)."""
+    out = layout()
+    st = getattr(lib, query)(ctypes.byref(cp), B, H, T, d, ctypes.byref(out))
+    return KiaError(st if st else 2, query)
+
+
+def _stream(stream, device):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream(device)
     return ctypes.c_void_p(s.cuda_stream)
 
 
@@ -114,26 +139,33 @@ def kia_workspace_layout_query(params: Params, B, H, T, d) -> KiaWorkspaceLayout
 
 def kia_forward(q, k, v, params: Params, o=None, stats=None, stream=None, events=None, idx_dump=None):
     """O = P V with K-interval weights.  Returns (o, stats); stats is a uint8
-    device buffer holding the forward -> backward state."""
+    device buffer holding the forward -> backward state.  Buffers passed in
+    (o, stats, idx_dump) are checked for device, dtype, shape or size."""
     torch = _torch()
     B, H, T, d = _shape(q)
+    dev = q.device
     for t, nm in ((q, "q"), (k, "k"), (v, "v")):
-        _check(t, nm, (B, H, T, d))
+        _check(t, nm, (B, H, T, d), dev)
     lib = _lib.load()
     cp = params.c()
     nbytes = int(lib.kia_stats_bytes(ctypes.byref(cp), B, H, T, d))
     if nbytes == 0:
-        raise KiaError(3 if d in (64, 128) else 2, "kia_stats_bytes")
+        raise _size_error(lib, "kia_stats_layout_query", cp, B, H, T, d, KiaStatsLayout)
     if o is None:
         o = torch.empty_like(q)
+    _check(o, "o", (B, H, T, d), dev)
     if stats is None:
-        stats = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    if idx_dump is not None and (idx_dump.dtype != torch.int32 or idx_dump.numel() != B * H * T * T):
-        raise ValueError("idx_dump must be int32 with B*H*T*T elements")
+        stats = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _buffer(stats, "stats", nbytes, dev)
+    if idx_dump is not None:
+        if idx_dump.dtype != torch.int32 or idx_dump.numel() != B * H * T * T:
+            raise ValueError("idx_dump must be int32 with B*H*T*T elements")
+        _buffer(idx_dump, "idx_dump", B * H * T * T * 4, dev)
     ext = _ext(events, idx_dump)
-    args = (ctypes.byref(cp), B, H, T, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-            stats.data_ptr(), stats.numel(), _stream(stream))
-    st = lib.kia_forward_ext(*args, ctypes.byref(ext)) if ext is not None else lib.kia_forward(*args)
+    with torch.cuda.device(dev):
+        args = (ctypes.byref(cp), B, H, T, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                stats.data_ptr(), _nbytes(stats), _stream(stream, dev))
+        st = lib.kia_forward_ext(*args, ctypes.byref(ext)) if ext is not None else lib.kia_forward(*args)
     if st:
         raise KiaError(st, "kia_forward")
     return o, stats
@@ -143,26 +175,33 @@ def kia_backward(q, k, v, o, do, stats, params: Params, dq=None, dk=None, dv=Non
                  stream=None, events=None):
     """dQ, dK, dV of sum(do * o).  Returns (dq, dk, dv, ws); ws is the
     workspace (uint8 device buffer) whose tiles kia_workspace_layout_query
-    describes."""
+    describes.  Buffers passed in are checked like kia_forward's."""
     torch = _torch()
     B, H, T, d = _shape(q)
+    dev = q.device
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
-        _check(t, nm, (B, H, T, d))
+        _check(t, nm, (B, H, T, d), dev)
     lib = _lib.load()
     cp = params.c()
+    sbytes = int(lib.kia_stats_bytes(ctypes.byref(cp), B, H, T, d))
     wbytes = int(lib.kia_workspace_bytes(ctypes.byref(cp), B, H, T, d))
-    if wbytes == 0:
-        raise KiaError(3, "kia_workspace_bytes")
+    if sbytes == 0 or wbytes == 0:
+        raise _size_error(lib, "kia_workspace_layout_query", cp, B, H, T, d, KiaWorkspaceLayout)
+    _buffer(stats, "stats", sbytes, dev)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
+    for t, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check(t, nm, (B, H, T, d), dev)
     if ws is None:
-        ws = torch.empty(wbytes, dtype=torch.uint8, device=q.device)
+        ws = torch.empty(wbytes, dtype=torch.uint8, device=dev)
+    _buffer(ws, "ws", wbytes, dev)
     ext = _ext(events, None)
-    args = (ctypes.byref(cp), B, H, T, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-            do.data_ptr(), stats.data_ptr(), stats.numel(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-            ws.data_ptr(), ws.numel(), _stream(stream))
-    st = lib.kia_backward_ext(*args, ctypes.byref(ext)) if ext is not None else lib.kia_backward(*args)
+    with torch.cuda.device(dev):
+        args = (ctypes.byref(cp), B, H, T, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                do.data_ptr(), stats.data_ptr(), _nbytes(stats), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                ws.data_ptr(), _nbytes(ws), _stream(stream, dev))
+        st = lib.kia_backward_ext(*args, ctypes.byref(ext)) if ext is not None else lib.kia_backward(*args)
     if st:
         raise KiaError(st, "kia_backward")
     return dq, dk, dv, ws
@@ -177,13 +216,21 @@ def kia_geometry(q, k, stats, params: Params, geo=None, stream=None):
     order of GEOMETRY_FIELDS."""
     torch = _torch()
     B, H, T, d = _shape(q)
-    _check(k, "k", (B, H, T, d))
+    dev = q.device
+    _check(q, "q", (B, H, T, d), dev)
+    _check(k, "k", (B, H, T, d), dev)
     lib = _lib.load()
+    cp = params.c()
+    sbytes = int(lib.kia_stats_bytes(ctypes.byref(cp), B, H, T, d))
+    if sbytes == 0:
+        raise _size_error(lib, "kia_stats_layout_query", cp, B, H, T, d, KiaStatsLayout)
+    _buffer(stats, "stats", sbytes, dev)
     if geo is None:
-        geo = torch.empty((len(GEOMETRY_FIELDS), B, H, T), dtype=torch.float32, device=q.device)
-    _check(geo, "geo")
-    st = lib.kia_geometry(ctypes.byref(params.c()), B, H, T, d, q.data_ptr(), k.data_ptr(), stats.data_ptr(),
-                          stats.numel(), geo.data_ptr(), geo.numel() * geo.element_size(), _stream(stream))
+        geo = torch.empty((len(GEOMETRY_FIELDS), B, H, T), dtype=torch.float32, device=dev)
+    _check(geo, "geo", (len(GEOMETRY_FIELDS), B, H, T), dev)
+    with torch.cuda.device(dev):
+        st = lib.kia_geometry(ctypes.byref(cp), B, H, T, d, q.data_ptr(), k.data_ptr(), stats.data_ptr(),
+                              _nbytes(stats), geo.data_ptr(), _nbytes(geo), _stream(stream, dev))
     if st:
         raise KiaError(st, "kia_geometry")
     return geo
@@ -194,10 +241,15 @@ def kia_tiles_to_dense(B, H, T, tiles, key_major: bool, dense=None, stream=None)
     dense [B, H, T, T] fp32 tensor; non-causal entries keep dense's content
     (zeros when dense is allocated here)."""
     torch = _torch()
+    dev = tiles.device
+    n_t = (T + 31) // 32
+    _buffer(tiles, "tiles", B * H * (n_t * (n_t + 1) // 2) * 32 * 32 * 4, dev)
     if dense is None:
-        dense = torch.zeros((B, H, T, T), dtype=torch.float32, device=tiles.device)
-    st = _lib.load().kia_tiles_to_dense(B, H, T, tiles.data_ptr(), 1 if key_major else 0,
-                                        dense.data_ptr(), _stream(stream))
+        dense = torch.zeros((B, H, T, T), dtype=torch.float32, device=dev)
+    _check(dense, "dense", (B, H, T, T), dev)
+    with torch.cuda.device(dev):
+        st = _lib.load().kia_tiles_to_dense(B, H, T, tiles.data_ptr(), 1 if key_major else 0,
+                                            dense.data_ptr(), _stream(stream, dev))
     if st:
         raise KiaError(st, "kia_tiles_to_dense")
     return dense
