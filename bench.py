@@ -231,6 +231,29 @@ def summarize_trace(d):
     return "\n".join(lines)
 
 
+def summarize_pmc(dirs):
+    """Markdown table of every counter in rocprofv3 --pmc csv runs (one run per
+    directory), mean per dispatch, one column per kernel."""
+    import csv
+    vals = {}
+    for d in dirs:
+        for r in csv.DictReader(open(_find_csv(d, "counter_collection.csv"))):
+            key = _kernel_key(r["Kernel_Name"])
+            if key is None:
+                continue
+            vals.setdefault(r["Counter_Name"], {}).setdefault(key, []).append(float(r["Counter_Value"]))
+    cols = [k for k in ("forward", "backward_rows", "backward_cols", "geometry")
+            if any(k in v for v in vals.values())]
+    lines = ["| counter | " + " | ".join(cols) + " |", "|---" * (len(cols) + 1) + "|"]
+    for name in sorted(vals):
+        cells = []
+        for k in cols:
+            x = vals[name].get(k)
+            cells.append("—" if not x else (f"{sum(x) / len(x):.4g}"))
+        lines.append(f"| {name} | " + " | ".join(cells) + " |")
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -253,7 +276,12 @@ def main():
                          "copy_write/) into profiles/traffic.json and a text summary")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="host only: print a markdown summary of a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--summarize-pmc", metavar="DIR", nargs="+",
+                    help="host only: print the per-kernel means of every counter in rocprofv3 --pmc runs")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        print(summarize_pmc(args.summarize_pmc))
+        return
     if args.ingest_pmc:
         ingest_pmc(args)
         return
