@@ -126,6 +126,23 @@ def test_bad_shapes_rejected():
         assert _fwd(lib, p, B=B, H=H, T=T, d=d) == 2
 
 
+@pytest.mark.parametrize("B,H,T", [(1 << 16, 1 << 16, 8),           # B*H past int32 (grid index)
+                                   (1 << 16, 1 << 10, 1 << 11),     # B*H*n_t workgroups past int32
+                                   (1 << 15, 1 << 15, 1 << 20)])    # score tiles past 9e18 bytes
+def test_oversized_shapes_rejected(B, H, T):
+    """Shapes whose grid or tile buffer would overflow the library's index
+    types are refused by every entry point, and size to zero."""
+    lib, mod = _lib()
+    p = _params(mod)
+    assert _fwd(lib, p, B=B, H=H, T=T) == 2
+    assert lib.kia_stats_bytes(ctypes.byref(p), B, H, T, 64) == 0
+    assert lib.kia_workspace_bytes(ctypes.byref(p), B, H, T, 64) == 0
+    ptrs = [A] * 10
+    q, k, v, o, do, st, dq, dk, dv, ws = ptrs
+    assert lib.kia_backward(ctypes.byref(p), B, H, T, 64, q, k, v, o, do, st, 1 << 40, dq, dk, dv, ws,
+                            1 << 40, None) == 2
+
+
 def test_null_misaligned_and_small_buffers_rejected():
     lib, mod = _lib()
     p = _params(mod)
