@@ -24,8 +24,13 @@ _INPUTS = {}
 
 def inputs(name):
     if name not in _INPUTS:
-        _INPUTS[name] = make_inputs(WORKLOADS[name])
+        _INPUTS[name] = make_inputs(_workload(name))
     return _INPUTS[name]
+
+
+def _workload(name):
+    """A named workload, or one defined in place (a Workload)."""
+    return name if isinstance(name, Workload) else WORKLOADS[name]
 
 
 def P(**kw):
@@ -54,7 +59,7 @@ def zero_sum_all_rows(g, params, tol=1e-5):
 
 def full_check(name, params, heads, rows=None, tail=None, zero_sum=None):
     q, k, v, do = inputs(name)
-    w = WORKLOADS[name]
+    w = _workload(name)
     print(f"[case] full-size {w.name} B{w.B} H{w.H} T{w.T} d{w.d} {params} slices {heads}", flush=True)
     g = run_gpu(q, k, v, do, params, want_dense=True, want_idx=False)
     p_or = to_oracle_params(params)
@@ -159,6 +164,22 @@ def test_c5_full_size(K, rule):
     w = WORKLOADS["c5"]
     full_check("c5", P(K=K, calibration="minmax", reconstruction="lerp", grad_rule=rule),
                [(0, [4, 64].index(K) * 5 + 2)], rows=_c5_rows, tail=w.T - 96)
+
+
+LONGEST = Workload("len32768", 1, 3, 32768, 64, "scaled", q_scale=2.0)
+
+
+def test_longest_rows_past_4gb_buffers():
+    """T = 32768 with three heads: 524,800 score tiles per head, so each of the
+    score, probability and gradient tile buffers holds 6.4 GB and the third
+    head's tiles start past 2^32 bytes (64-bit tile offsets throughout).
+    Sampled rows across the sequence (tile and block edges included) and the
+    last 96 keys' dK / dV of every head against the oracle; the zero row sum
+    over all 98,304 rows."""
+    T = LONGEST.T
+    rows = [0, 1, 31, 32, 127, 128, 4095, 16383, 16384, 24577, 32000, T - 97]
+    full_check(LONGEST, P(K=32, calibration="minmax", reconstruction="lerp"), [(0, 0), (0, 2)],
+               rows=rows, tail=T - 96)
 
 
 # ---------------------------------------------------------------------------
