@@ -251,6 +251,13 @@ class SliceCheck:
                 self.idx_checked += int(ok.sum())
                 self.idx_mismatch += int((gi[ok] != ri[ok]).sum())
 
+        if p.grad_rule == O.P1:
+            # P1 subtracts the row mean of the detached gradient over all t+1
+            # causal keys: a decision that moves one key's dS in row t moves
+            # the mean, and with it dS at every key j <= t
+            for t in np.flatnonzero(self.amb_bwd):
+                self.amb_keys_bwd.update(range(int(t) + 1))
+
     def _rounding_band(self, t, fw, sg):
         """Rounded-exponential baselines: a key whose exp(s - m) lies closer to
         a rounding midpoint of the format than the two sides' exponentials can

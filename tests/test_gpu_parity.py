@@ -78,6 +78,14 @@ def test_small_d128(cal, rec, ste):
     check(SMALL128, P(K=16, tau=6.0, calibration=cal, reconstruction=rec, surrogate=ste))
 
 
+@pytest.mark.parametrize("cal,rec,ste", [("minmax", "lerp", "weight"), ("fwm", "nearest", "prob")])
+@pytest.mark.parametrize("rule", RULES)
+def test_small_d128_rules(cal, rec, ste, rule):
+    """Every gradient rule at d = 128 (the P1 prefix sums and centring have
+    their own per-d code)."""
+    check(SMALL128, P(K=16, tau=6.0, calibration=cal, reconstruction=rec, surrogate=ste, grad_rule=rule))
+
+
 @pytest.mark.parametrize("T", [1, 2, 31, 32, 33, 64, 97])
 def test_edge_lengths(T):
     w = Workload(f"len{T}", 1, 3, T, 64, "scaled", q_scale=2.0)
