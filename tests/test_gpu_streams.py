@@ -17,6 +17,7 @@ from workloads import Workload, make_inputs
 pytestmark = pytest.mark.gpu
 
 W = Workload("streams", 2, 3, 200, 64, "scaled", q_scale=2.0)
+W128 = Workload("streams_d128", 1, 2, 150, 128, "head_temp", lo=0.5, hi=3.0)
 
 
 def _params(**kw):
@@ -24,9 +25,9 @@ def _params(**kw):
     return Params(**kw)
 
 
-def _tensors(seed_shift=0):
+def _tensors(seed_shift=0, w=W):
     import torch
-    q, k, v, do = make_inputs(W)
+    q, k, v, do = make_inputs(w)
     if seed_shift:
         q = np.roll(q, seed_shift, axis=2)
     dev = torch.device("cuda:0")
@@ -50,15 +51,22 @@ def _alloc(kia, x, p):
 
 
 VARIANTS = [dict(K=32), dict(K=4, calibration="fwm", reconstruction="nearest", surrogate="prob"),
-            dict(K=4, grad_rule="p1"), dict(K=1, reconstruction="exp_fp8")]
+            dict(K=4, grad_rule="p1"), dict(K=1, reconstruction="exp_fp8"), dict(K=16, d128=True),
+            dict(K=4, calibration="fwm", reconstruction="nearest", surrogate="prob", grad_rule="p1", d128=True)]
+
+
+def _variant(kw):
+    """Params and workload of a variant (d128 selects the d = 128 workload)."""
+    kw = dict(kw)
+    return _params(**{k: v for k, v in kw.items() if k != "d128"}), (W128 if kw.get("d128") else W)
 
 
 @pytest.mark.parametrize("kw", VARIANTS, ids=lambda kw: "-".join(f"{k}={v}" for k, v in kw.items()))
 def test_side_stream_matches_current_stream(kw):
     import torch
     import quantized_softmax_attention_amd as kia
-    p = _params(**kw)
-    x = _tensors()
+    p, w = _variant(kw)
+    x = _tensors(w=w)
     a, b = _alloc(kia, x, p), _alloc(kia, x, p)
     print(f"[case] side stream {p}", flush=True)
     _step(kia, x, p, a)
@@ -74,9 +82,9 @@ def test_side_stream_matches_current_stream(kw):
 def test_graph_replays_match_eager(kw):
     import torch
     import quantized_softmax_attention_amd as kia
-    p = _params(**kw)
-    x = _tensors()
-    other = _tensors(seed_shift=17)
+    p, w = _variant(kw)
+    x = _tensors(w=w)
+    other = _tensors(seed_shift=17, w=w)
     eager = _alloc(kia, x, p)
     print(f"[case] graph capture {p}", flush=True)
     _step(kia, x, p, eager)
@@ -111,8 +119,8 @@ def test_autograd_op_matches_direct_calls(kw):
     torch.autograd, exactly kia_backward's dQ, dK, dV."""
     import torch
     import quantized_softmax_attention_amd as kia
-    p = _params(**kw)
-    q, k, v, do = _tensors()
+    p, w = _variant(kw)
+    q, k, v, do = _tensors(w=w)
     print(f"[case] autograd op {p}", flush=True)
     o_ref, st = kia.kia_forward(q, k, v, p)
     dq_ref, dk_ref, dv_ref, _ = kia.kia_backward(q, k, v, o_ref, do, st, p)
