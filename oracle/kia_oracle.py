@@ -76,7 +76,9 @@ Readings where the pages leave a step open:
 
 Parity: every function below is pinned by the CPU tests (closed forms,
 brute force, finite differences, an autograd re-expression, the softmax
-limit, the zero-sum identity); none is "parity unpinned".
+limit, the zero-sum identity; the whole-tensor forward / backward against the
+per-head functions on slices that all differ, with planted index swaps; the
+per-key decision override against closed forms); none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -115,9 +117,14 @@ class Params:
 # ---------------------------------------------------------------------------
 
 def row_scores(q_t: np.ndarray, keys: np.ndarray) -> np.ndarray:
-    """s_j = Q_t . K_j / sqrt(d) over the causal keys (reading R7)."""
+    """s_j = Q_t . K_j / sqrt(d) over the causal keys (reading R7).
+
+    Each key's dot product is summed by itself, in the same order for every
+    key (not by a matrix-vector product, whose blocking can round equal rows
+    differently), so equal keys get bitwise-equal scores and the lowest-index
+    tie rule (R3) applies to them."""
     d = keys.shape[1]
-    return (keys.astype(np.float64) @ q_t.astype(np.float64)) / np.sqrt(d)
+    return (keys.astype(np.float64) * q_t.astype(np.float64)).sum(axis=1) / np.sqrt(d)
 
 
 @dataclass
@@ -166,12 +173,20 @@ class Recon:
     wN: np.ndarray     # Nearest weights
 
 
-def reconstruct(s: np.ndarray, m: float, h: float, p: Params, clamp: bool = True) -> Recon:
+def reconstruct(s: np.ndarray, m: float, h: float, p: Params, clamp: bool = True,
+                decisions: dict | None = None) -> Recon:
     """Grid reconstruction of a row (section 3 "Reconstruction"; App. A).
 
     ``clamp=False`` keeps u unclamped and lets the end segments extend
     linearly; it exists for derivative checks that move a score past the row
     extremes while the extremes are held fixed.
+
+    ``decisions`` (test use) maps a key index to the integer decision taken
+    for it instead of rounding this row's own u: the LERP segment i (LERP) or
+    the Nearest point r (Nearest), or -1 for "outside the FWM window".  A
+    decision that is taken in floating point (floor, the window test) can go
+    either way for a key whose u lies within rounding of the boundary; this
+    evaluates the same operator, in fp64 from the same u, on the other side.
     """
     K = p.K
     u = (m - s) / h
@@ -189,6 +204,16 @@ def reconstruct(s: np.ndarray, m: float, h: float, p: Params, clamp: bool = True
         uc = np.minimum(u, float(K)) if clamp else u.copy()
         i = np.clip(np.floor(uc), 0, K - 1).astype(np.int64)      # R2
         r = np.clip(np.floor(uc + 0.5), 0, K).astype(np.int64)    # R1
+    for j, level in (decisions or {}).items():
+        if level < 0:
+            mask[j] = 0.0
+            continue
+        if p.calibration == FWM:
+            mask[j] = 1.0
+        if p.reconstruction == LERP:
+            i[j] = level
+        else:
+            r[j] = level
     f = uc - i
     gi, gi1 = np.exp(-h * i), np.exp(-h * (i + 1))
     wL = mask * ((1.0 - f) * gi + f * gi1)                      # linear interpolation
@@ -223,19 +248,40 @@ class RowForward:
     WL: float
 
 
-def row_forward(s: np.ndarray, p: Params) -> RowForward:
+def format_neighbours(x: np.ndarray, frac_bits: int, emin: int):
+    """The two adjacent values of the format that bracket each x >= 0 (lower,
+    upper; equal when x is representable), with the same quantum as
+    round_to_format."""
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)
+    quantum = np.ldexp(1.0, np.maximum(e - 1, emin) - frac_bits)
+    lo = np.floor(x / quantum) * quantum
+    hi = np.ceil(x / quantum) * quantum
+    return lo, hi
+
+
+def row_forward(s: np.ndarray, p: Params, decisions: dict | None = None) -> RowForward:
+    """Forward of one causal row.  ``decisions`` (test use) fixes the integer
+    decisions at the listed keys: grid operators as in reconstruct; for the
+    rounded exponentials 1 takes the format value above exp(s - m) and 0 the
+    one below, instead of rounding to the nearer."""
     cal = calibrate(s, p)
     if p.reconstruction in EXP_FAMILY:                         # R12, R14: softmax
         w = np.exp(s - cal.m)
         if p.reconstruction in FORMATS:
-            w = round_to_format(w, *FORMATS[p.reconstruction])
+            e = w
+            w = round_to_format(e, *FORMATS[p.reconstruction])
+            if decisions:
+                lo, hi = format_neighbours(e, *FORMATS[p.reconstruction])
+                for j, up in decisions.items():
+                    w[j] = hi[j] if up else lo[j]
         W = float(w.sum())
         return RowForward(s, cal, None, w, W, w / W, w, W)
     if cal.degenerate:                                          # R4
         w = np.ones_like(s)
         W = float(w.sum())
         return RowForward(s, cal, None, w, W, w / W, w, W)
-    rec = reconstruct(s, cal.m, cal.h, p)
+    rec = reconstruct(s, cal.m, cal.h, p, decisions=decisions)
     w = rec.wL if p.reconstruction == LERP else rec.wN          # Nearest computed directly
     W = float(w.sum())
     WL = float(rec.wL.sum())

@@ -111,8 +111,8 @@ MUTANTS = [
      "dV[: t + 1] += np.outer(fw.P, dO64[t])", "dV[: t + 1] += np.outer(fw.wL / fw.WL, dO64[t])",
      lambda m: check_autograd(m, m.Params(K=4, reconstruction=m.NEAREST), *_head_inputs(T=12, d=6))),
     ("score scale dropped",
-     "return (keys.astype(np.float64) @ q_t.astype(np.float64)) / np.sqrt(d)",
-     "return (keys.astype(np.float64) @ q_t.astype(np.float64))",
+     "return (keys.astype(np.float64) * q_t.astype(np.float64)).sum(axis=1) / np.sqrt(d)",
+     "return (keys.astype(np.float64) * q_t.astype(np.float64)).sum(axis=1)",
      lambda m: check_autograd(m, m.Params(K=4), *_head_inputs(T=12, d=6))),
     ("untruncated step keeps FWM's zero tail",
      "        mask = np.ones_like(u)\n    g = grid(h, K)", "        mask = (u <= K).astype(np.float64)\n    g = grid(h, K)",

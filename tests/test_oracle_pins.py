@@ -481,3 +481,18 @@ def test_rounded_exponential_zero_sum_under_full_only(rec):
     det = O.row_backward(O.row_forward(s, pd), dP, pd)
     # the rounding leaves sum_j P_j dP_j - delta * sum_j e_j / W != 0 under detach
     assert abs(det.dS.sum()) > 1e-6 * np.abs(det.dS).sum()
+
+
+def test_equal_keys_score_equally():
+    """Equal keys get bitwise-equal scores wherever they sit in the row, so
+    the lowest-index rule decides their ties (reading R3)."""
+    rng = np.random.default_rng(12)
+    for d in (5, 64, 128):
+        keys = (rng.standard_normal((700, d)) * 0.2).astype(np.float32)
+        keys[[3, 64, 65, 333, 699]] = rng.standard_normal(d).astype(np.float32)
+        q = rng.standard_normal(d).astype(np.float32)
+        s = O.row_scores(q, keys)
+        assert len(set(s[[3, 64, 65, 333, 699]].tolist())) == 1
+        q_max = keys[3] * 10
+        cal = O.calibrate(O.row_scores(q_max, keys), Params(K=4))
+        assert cal.a == 3
