@@ -159,8 +159,10 @@ kia_status kia_backward(const kia_params* p, int B, int H, int T, int d,
  * key prefix-sum and row-centring launches).  idx_dump (forward only): NULL
  * or int32 [B,H,T,T]; for every causal pair the kernel writes the grid index
  * it used (the LERP segment, or the Nearest grid point), -1 for keys outside
- * the FWM window, 0 under KIA_REC_EXACT and the rounded baselines (no grid);
- * non-causal entries are left untouched. */
+ * the FWM window; 0 under KIA_REC_EXACT (no grid); under the rounded
+ * baselines the fp32 bit pattern of the rounded exponential, i.e. which of
+ * the format's values the rounding chose; non-causal entries are left
+ * untouched. */
 typedef struct kia_ext {
     void* const* events;
     int32_t n_events;

@@ -228,9 +228,12 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
         const float s = sv[r];
         if (softmax_rec(REC)) {
             // exact-softmax reference w = exp(s - m), or its rounded baselines
-            w[r] = valid ? round_exp<REC>(fast_exp2((s - rg.m) * kLog2e)) : 0.f;
+            const float we = round_exp<REC>(fast_exp2((s - rg.m) * kLog2e));
+            w[r] = valid ? we : 0.f;
             Wt += w[r];
-            if (DUMP && qvalid && valid) a.idx_dump[((size_t)bh * T + qrow) * T + key] = 0;
+            // the dump records the rounded value's fp32 bits (0 for the exact reference)
+            if (DUMP && qvalid && valid)
+                a.idx_dump[((size_t)bh * T + qrow) * T + key] = (REC == REC_EXACT) ? 0 : __float_as_int(we);
             return;
         }
         const float u = (rg.m - s) * rg.invh;

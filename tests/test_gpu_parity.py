@@ -22,22 +22,30 @@ def P(**kw):
     return Params(**kw)
 
 
-def check(w: Workload, params, heads=None, max_amb_frac=0.02, verbose=True):
-    q, k, v, do = make_inputs(w)
+MIN_COVERAGE = 0.95    # share of each slice's rows (O, dQ) and keys (dK, dV) a check must compare
+
+
+def check(w: Workload, params, heads=None, max_amb_frac=0.02, verbose=True, inputs=None):
+    q, k, v, do = inputs if inputs is not None else make_inputs(w)
     print(f"[case] {w.name} B{w.B} H{w.H} T{w.T} d{w.d} {params}", flush=True)
     g = run_gpu(q, k, v, do, params)
     p_or = to_oracle_params(params)
     heads = heads or [(b, h) for b in range(w.B) for h in range(w.H)]
     worst = {}
     n_amb = 0
+    low = []
     for (b, h) in heads:
         sc = SliceCheck(q, k, v, do, p_or, g, b, h)
         assert sc.score_viol == 0, f"scores outside the fp32 bound in slice {(b, h)}"
         assert sc.idx_mismatch == 0, f"{sc.idx_mismatch} grid indices differ in slice {(b, h)}"
         for name in ("O", "dQ", "dK", "dV"):
-            err, kept = sc.compare(name)
+            err, kept, region = sc.compare(name)
             worst[name] = max(worst.get(name, 0.0), err)
-            assert err <= TOL, f"{name} rel err {err:.3e} in slice {(b, h)} ({kept} rows compared)"
+            assert err <= TOL, f"{name} rel err {err:.3e} in slice {(b, h)} ({kept} of {region} compared)"
+            if region >= 64:
+                assert kept >= MIN_COVERAGE * region, f"{name} compared on {kept} of {region} in slice {(b, h)}"
+            if kept < region:
+                low.append((name, (b, h), kept, region))
         if params.grad_rule in ("full", "p1"):
             bad = sc.zero_sum_violations(q, k, v, do, b, h)
             assert not bad, f"zero-sum violated in slice {(b, h)}: {bad[:3]}"
@@ -45,7 +53,7 @@ def check(w: Workload, params, heads=None, max_amb_frac=0.02, verbose=True):
     pairs = len(heads) * w.T * (w.T + 1) // 2
     assert n_amb <= max_amb_frac * pairs
     if verbose:
-        print(f"  worst rel err {worst}  ambiguous pairs {n_amb}/{pairs}", flush=True)
+        print(f"  worst rel err {worst}  boundary-near pairs {n_amb}/{pairs}  partial checks {low[:6]}", flush=True)
     return g, worst
 
 
@@ -122,3 +130,48 @@ def test_small_untruncated_narrow_step(rec):
     """The untruncated step with tau = 0.5, K = 2: the grid runs tens of
     intervals below the window, far past the K of the truncated operator."""
     check(SMALL, P(K=2, tau=0.5, calibration="fwm_untrunc", reconstruction=rec))
+
+
+# ---------------------------------------------------------------------------
+# degenerate and near-degenerate row spans (App. A, Table S1: separate
+# branches for spans below and above 1e-12)
+# ---------------------------------------------------------------------------
+
+def degenerate_inputs(d, T=70, seed=21):
+    """Four heads of rows with zero or tiny score spans, beside ordinary rows:
+      head 0: every third query row t >= 1 is zero, so all its scores are 0
+              (span exactly 0 with t + 1 keys);
+      head 1: keys 0..23 are one repeated vector, so rows 1..23 score every
+              key identically (span exactly 0);
+      head 2: query rows scaled by 1e-11 / 1e-9 / 1e-6 in turn (spans of
+              about that size, above the threshold: the ordinary branch with
+              a grid a few 1e-12 to 1e-7 nats wide);
+      head 3: ordinary rows (spans of a few nats) for comparison."""
+    rng = np.random.default_rng(seed)
+    q, k, v, do = (rng.standard_normal((1, 4, T, d)) for _ in range(4))
+    q *= 2.0
+    q[0, 0, 3::3] = 0.0
+    k[0, 1, 1:24] = k[0, 1, 0]
+    q[0, 2, 0::3] *= 1e-11
+    q[0, 2, 1::3] *= 1e-9
+    q[0, 2, 2::3] *= 1e-6
+    return tuple(x.astype(np.float32) for x in (q, k, v, do))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("rec,ste", [("lerp", "weight"), ("nearest", "weight"), ("nearest", "prob")])
+@pytest.mark.parametrize("rule", RULES)
+def test_degenerate_spans(d, rec, ste, rule):
+    """Rows with span exactly 0 take the degenerate branch (uniform P over the
+    causal keys, softmax-limit backward P (dP - delta), no calibration terms);
+    rows with spans of 1e-11 to 1e-6 take the ordinary branch with a very fine
+    grid.  O, dQ, dK, dV against the oracle, every output finite."""
+    w = Workload(f"degenerate_d{d}", 1, 4, 70, d, "plain")
+    q, k, v, do = degenerate_inputs(d)
+    p = P(K=4, calibration="minmax", reconstruction=rec, surrogate=ste, grad_rule=rule)
+    g, _ = check(w, p, inputs=(q, k, v, do))
+    for key in ("O", "dQ", "dK", "dV"):
+        assert bool(g[key].isfinite().all()), key
+    span = (g["m"] - g["n"]).cpu().numpy()[0]
+    assert (span[0, 3::3] == 0).all() and (span[1, 1:24] == 0).all()
+    assert (span[2, 1:] > 1e-12).all()
