@@ -51,7 +51,8 @@ typedef enum kia_status {
     KIA_ERR_PARAM = 3,     /* flag out of range, n_intervals < 1, tau <= 0 under FWM / FWM_UNTRUNC */
     KIA_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned */
     KIA_ERR_BUFFER = 5,    /* stats or workspace smaller than the size query returns */
-    KIA_ERR_HIP = 6        /* a kernel launch failed */
+    KIA_ERR_HIP = 6,       /* a kernel launch failed */
+    KIA_ERR_SCRATCH = 7    /* kia_backward_noalloc: one (b, h) slice's workspace exceeds its scratch */
 } kia_status;
 
 enum { KIA_CAL_MINMAX = 0, KIA_CAL_FWM = 1, KIA_CAL_FWM_UNTRUNC = 2 };
@@ -151,6 +152,26 @@ kia_status kia_backward(const kia_params* p, int B, int H, int T, int d,
                         const void* stats, size_t stats_bytes,
                         float* dq, float* dk, float* dv,
                         void* ws, size_t ws_bytes, void* stream);
+
+/* Backward without any allocation, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The same computation and results as kia_backward, with
+ * the workspace taken from a static device array the library holds on each
+ * device it runs on: KIA_NOALLOC_SCRATCH_MIB MiB per device, kept until the
+ * process ends.  Batches whose workspace exceeds it run in consecutive
+ * groups of (b, h) slices on `stream`; a shape whose single slice needs more
+ * than the scratch (e.g. T = 8192 at any d) returns KIA_ERR_SCRATCH before
+ * any launch.  The call allocates nothing (no hipMalloc, no library
+ * allocation); the first call on a device looks the array up once.  Every
+ * call on one device shares that device's array: calls that overlap in time
+ * on one device (other streams, other threads) race and give undefined
+ * results.  Arguments and the other errors are those of kia_backward. */
+#define KIA_NOALLOC_SCRATCH_MIB 256
+kia_status kia_backward_noalloc(const kia_params* p, int B, int H, int T, int d,
+                                const float* q, const float* k, const float* v,
+                                const float* o, const float* d_o,
+                                const void* stats, size_t stats_bytes,
+                                float* dq, float* dk, float* dv, void* stream);
 
 /* Optional extras for the two calls above.  events: NULL or an array of
  * hipEvent_t (as void*) recorded on `stream` around each kernel: forward

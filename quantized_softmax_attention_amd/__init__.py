@@ -207,6 +207,36 @@ def kia_backward(q, k, v, o, do, stats, params: Params, dq=None, dk=None, dv=Non
     return dq, dk, dv, ws
 
 
+def kia_backward_noalloc(q, k, v, o, do, stats, params: Params, dq=None, dk=None, dv=None, stream=None):
+    """kia_backward without a workspace: the library takes it from its own
+    per-device scratch (include/kia.h, kia_backward_noalloc) and allocates
+    nothing.  Output buffers not passed in are allocated here, by the caller's
+    side.  Returns (dq, dk, dv)."""
+    torch = _torch()
+    B, H, T, d = _shape(q)
+    dev = q.device
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (do, "do")):
+        _check(t, nm, (B, H, T, d), dev)
+    lib = _lib.load()
+    cp = params.c()
+    sbytes = int(lib.kia_stats_bytes(ctypes.byref(cp), B, H, T, d))
+    if sbytes == 0:
+        raise _size_error(lib, "kia_stats_layout_query", cp, B, H, T, d, KiaStatsLayout)
+    _buffer(stats, "stats", sbytes, dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for t, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check(t, nm, (B, H, T, d), dev)
+    with torch.cuda.device(dev):
+        st = lib.kia_backward_noalloc(ctypes.byref(cp), B, H, T, d, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                      o.data_ptr(), do.data_ptr(), stats.data_ptr(), _nbytes(stats),
+                                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), _stream(stream, dev))
+    if st:
+        raise KiaError(st, "kia_backward_noalloc")
+    return dq, dk, dv
+
+
 GEOMETRY_FIELDS = ("span", "h", "q_norm", "k_norm", "entropy_p", "entropy_soft", "tv", "top_mass")
 
 

@@ -5,9 +5,20 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+#include <mutex>
+
 #include "../../include/kia.h"
 #include "kia_common.hpp"
 #include "kia_kernels.hpp"
+
+// Device scratch of the allocation-free backward (kia_backward_noalloc): it
+// stands in for kia_backward's caller-supplied workspace.  Each device the
+// library runs on holds its own copy until the process ends.  Host code
+// addresses it only through the per-device pointer hipGetSymbolAddress
+// returns; the array's name is a host-side stand-in, not a device address.
+constexpr size_t kScratchBytes = (size_t)KIA_NOALLOC_SCRATCH_MIB << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -193,62 +204,145 @@ kia_status kia_forward(const kia_params* p, int B, int H, int T, int d, const fl
     return kia_forward_ext(p, B, H, T, d, q, k, v, o, stats, stats_bytes, stream, nullptr);
 }
 
+}  // extern "C"
+
+namespace {
+
+struct BwdPtrs {
+    const float *q, *k, *v, *o, *d_o;
+    const void* stats;
+    size_t stats_bytes;
+    float *dq, *dk, *dv;
+};
+
+// Checks shared by the backward entry points (everything but the workspace).
+kia_status check_backward(const kia_params* p, int B, int H, int T, int d, const BwdPtrs& b, Shape* s) {
+    kia_status st = check_params(p);
+    if (st != KIA_OK) return st;
+    if ((st = check_shape(B, H, T, d, s)) != KIA_OK) return st;
+    if (!b.q || !b.k || !b.v || !b.o || !b.d_o || !b.stats || !b.dq || !b.dk || !b.dv) return KIA_ERR_NULL;
+    if (!aligned16(b.q) || !aligned16(b.k) || !aligned16(b.v) || !aligned16(b.o) || !aligned16(b.d_o) ||
+        !aligned16(b.stats) || !aligned16(b.dq) || !aligned16(b.dk) || !aligned16(b.dv))
+        return KIA_ERR_ALIGN;
+    kia_stats_layout L;
+    stats_layout(p, *s, &L);
+    if (b.stats_bytes < L.total_bytes) return KIA_ERR_BUFFER;
+    return KIA_OK;
+}
+
+// Shape of `n` of the slices of s (the same T and d).
+Shape slices_of(const Shape& s, int64_t n) {
+    Shape c = s;
+    c.BH = n;
+    c.B = 1;
+    c.H = n;
+    return c;
+}
+
+// Launch the backward over the slices [s0, s0 + n) of a checked shape s.  The
+// inputs, outputs and the forward's statistics are addressed inside the
+// whole-batch buffers; `ws` holds the workspace laid out for n slices.
+// Slices never interact, so any split of the batch gives the same results.
+kia_status run_backward(const kia_params* p, const Shape& s, int64_t s0, int64_t n, const BwdPtrs& b, char* ws,
+                        const kia_ext* ext, hipStream_t hs) {
+    const bool p1 = p->grad_rule == KIA_GRAD_P1;
+    if (p1 && n * s.tiles_per_head > INT32_MAX) return KIA_ERR_SHAPE;  // one-dimensional grid of the centring kernel
+    kia_stats_layout L;
+    stats_layout(p, s, &L);
+    const Shape c = slices_of(s, n);
+    kia_workspace_layout WL;
+    workspace_layout(p, c, &WL);
+
+    const size_t rows0 = (size_t)(s0 * s.T);               // first row of the range
+    const size_t elem0 = rows0 * (size_t)s.d;              // first element of a [B, H, T, d] tensor
+    const size_t tile0 = (size_t)s0 * (size_t)s.tiles_per_head * kia::kTileElems;
+    const char* sb = (const char*)b.stats;
+    kia::BwdArgs a;
+    a.q = b.q + elem0; a.k = b.k + elem0; a.v = b.v + elem0; a.o = b.o + elem0; a.d_o = b.d_o + elem0;
+    a.tiles = (const float*)(sb + L.scores) + tile0;
+    a.row_m = (const float*)(sb + L.row_m) + rows0;
+    a.row_n = (const float*)(sb + L.row_n) + rows0;
+    a.row_a = (const int32_t*)(sb + L.row_a) + rows0;
+    a.row_b = (const int32_t*)(sb + L.row_b) + rows0;
+    a.row_w = (const float*)(sb + L.row_w) + rows0;
+    a.row_wl = (const float*)(sb + L.row_wl) + rows0;
+    a.o_lerp = prob_extras(p) ? (const float*)(sb + L.o_lerp) + elem0 : nullptr;
+    a.dq = b.dq + elem0; a.dk = b.dk + elem0; a.dv = b.dv + elem0;
+    a.probs = (float*)(ws + WL.probs);
+    a.dscores = (float*)(ws + WL.dscores);
+    a.row_cm = (float*)(ws + WL.row_cm);
+    a.row_cn = (float*)(ws + WL.row_cn);
+    a.prefix_k = p1 ? (float*)(ws + WL.prefix_k) : nullptr;
+    a.chunk_k = p1 ? (float*)(ws + WL.chunk_k) : nullptr;
+    a.BH = (int)n; a.T = (int)s.T; a.n_t = (int)s.n_t; a.K = p->n_intervals;
+    a.tau = tau_of(p);
+    a.scale = 1.f / sqrtf((float)s.d);
+    a.rule = p->grad_rule;
+
+    kia_status st;
+    const kia::FwdConfig cfg = config_of(p, (int)s.d, false);
+    if ((st = record(ext, 0, hs)) != KIA_OK) return st;
+    if (p1 && kia::launch_key_prefix((int)s.d, a, hs) != hipSuccess) return KIA_ERR_HIP;
+    if (kia::launch_backward_rows(cfg, a, hs) != hipSuccess) return KIA_ERR_HIP;
+    if (p1 && kia::launch_center_rows(a, hs) != hipSuccess) return KIA_ERR_HIP;
+    if ((st = record(ext, 1, hs)) != KIA_OK) return st;
+    if ((st = record(ext, 2, hs)) != KIA_OK) return st;
+    if (kia::launch_backward_cols((int)s.d, a, hs) != hipSuccess) return KIA_ERR_HIP;
+    return record(ext, 3, hs);
+}
+
+// ---- the allocation-free backward -----------------------------------------
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch: looked up once per device (with the device
+// current), then reused.
+kia_status device_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KIA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return KIA_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return KIA_OK;
+}
+
+// Most slices whose workspace fits the scratch (0 when one slice does not).
+int64_t slices_per_scratch(const kia_params* p, const Shape& s) {
+    kia_workspace_layout WL;
+    workspace_layout(p, slices_of(s, 1), &WL);
+    if (WL.total_bytes > kScratchBytes) return 0;
+    int64_t n = std::min<int64_t>(s.BH, (int64_t)(kScratchBytes / WL.total_bytes));
+    for (; n > 1; --n) {
+        workspace_layout(p, slices_of(s, n), &WL);
+        if (WL.total_bytes <= kScratchBytes) break;
+    }
+    return n;
+}
+
+}  // namespace
+
+extern "C" {
+
 kia_status kia_backward_ext(const kia_params* p, int B, int H, int T, int d, const float* q, const float* k,
                             const float* v, const float* o, const float* d_o, const void* stats,
                             size_t stats_bytes, float* dq, float* dk, float* dv, void* ws, size_t ws_bytes,
                             void* stream, const kia_ext* ext) {
-    kia_status st = check_params(p);
-    if (st != KIA_OK) return st;
+    const BwdPtrs b = {q, k, v, o, d_o, stats, stats_bytes, dq, dk, dv};
     Shape s;
-    if ((st = check_shape(B, H, T, d, &s)) != KIA_OK) return st;
-    if (!q || !k || !v || !o || !d_o || !stats || !dq || !dk || !dv || !ws) return KIA_ERR_NULL;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(d_o) ||
-        !aligned16(stats) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(ws))
-        return KIA_ERR_ALIGN;
-    kia_stats_layout L;
-    stats_layout(p, s, &L);
-    if (stats_bytes < L.total_bytes) return KIA_ERR_BUFFER;
+    kia_status st = check_backward(p, B, H, T, d, b, &s);
+    if (st != KIA_OK) return st;
+    if (!ws) return KIA_ERR_NULL;
+    if (!aligned16(ws)) return KIA_ERR_ALIGN;
     kia_workspace_layout WL;
     workspace_layout(p, s, &WL);
     if (ws_bytes < WL.total_bytes) return KIA_ERR_BUFFER;
     if (ext && ext->n_events < 0) return KIA_ERR_PARAM;
-
-    const char* sb = (const char*)stats;
-    char* wb = (char*)ws;
-    kia::BwdArgs a;
-    a.q = q; a.k = k; a.v = v; a.o = o; a.d_o = d_o;
-    a.tiles = (const float*)(sb + L.scores);
-    a.row_m = (const float*)(sb + L.row_m);
-    a.row_n = (const float*)(sb + L.row_n);
-    a.row_a = (const int32_t*)(sb + L.row_a);
-    a.row_b = (const int32_t*)(sb + L.row_b);
-    a.row_w = (const float*)(sb + L.row_w);
-    a.row_wl = (const float*)(sb + L.row_wl);
-    a.o_lerp = prob_extras(p) ? (const float*)(sb + L.o_lerp) : nullptr;
-    a.dq = dq; a.dk = dk; a.dv = dv;
-    a.probs = (float*)(wb + WL.probs);
-    a.dscores = (float*)(wb + WL.dscores);
-    a.row_cm = (float*)(wb + WL.row_cm);
-    a.row_cn = (float*)(wb + WL.row_cn);
-    const bool p1 = p->grad_rule == KIA_GRAD_P1;
-    if (p1 && s.BH * s.tiles_per_head > INT32_MAX) return KIA_ERR_SHAPE;  // one-dimensional grid of the centring kernel
-    a.prefix_k = p1 ? (float*)(wb + WL.prefix_k) : nullptr;
-    a.chunk_k = p1 ? (float*)(wb + WL.chunk_k) : nullptr;
-    a.BH = (int)s.BH; a.T = T; a.n_t = (int)s.n_t; a.K = p->n_intervals;
-    a.tau = tau_of(p);
-    a.scale = 1.f / sqrtf((float)d);
-    a.rule = p->grad_rule;
-
-    hipStream_t hs = (hipStream_t)stream;
-    const kia::FwdConfig c = config_of(p, d, false);
-    if ((st = record(ext, 0, hs)) != KIA_OK) return st;
-    if (p1 && kia::launch_key_prefix(d, a, hs) != hipSuccess) return KIA_ERR_HIP;
-    if (kia::launch_backward_rows(c, a, hs) != hipSuccess) return KIA_ERR_HIP;
-    if (p1 && kia::launch_center_rows(a, hs) != hipSuccess) return KIA_ERR_HIP;
-    if ((st = record(ext, 1, hs)) != KIA_OK) return st;
-    if ((st = record(ext, 2, hs)) != KIA_OK) return st;
-    if (kia::launch_backward_cols(d, a, hs) != hipSuccess) return KIA_ERR_HIP;
-    return record(ext, 3, hs);
+    return run_backward(p, s, 0, s.BH, b, (char*)ws, ext, (hipStream_t)stream);
 }
 
 kia_status kia_backward(const kia_params* p, int B, int H, int T, int d, const float* q, const float* k,
@@ -256,6 +350,25 @@ kia_status kia_backward(const kia_params* p, int B, int H, int T, int d, const f
                         float* dq, float* dk, float* dv, void* ws, size_t ws_bytes, void* stream) {
     return kia_backward_ext(p, B, H, T, d, q, k, v, o, d_o, stats, stats_bytes, dq, dk, dv, ws, ws_bytes,
                             stream, nullptr);
+}
+
+kia_status kia_backward_noalloc(const kia_params* p, int B, int H, int T, int d, const float* q, const float* k,
+                                const float* v, const float* o, const float* d_o, const void* stats,
+                                size_t stats_bytes, float* dq, float* dk, float* dv, void* stream) {
+    const BwdPtrs b = {q, k, v, o, d_o, stats, stats_bytes, dq, dk, dv};
+    Shape s;
+    kia_status st = check_backward(p, B, H, T, d, b, &s);
+    if (st != KIA_OK) return st;
+    const int64_t per = slices_per_scratch(p, s);
+    if (per < 1) return KIA_ERR_SCRATCH;
+    void* ws = nullptr;
+    if ((st = device_scratch(&ws)) != KIA_OK) return st;
+    // every workspace entry is written before it is read: nothing to clear
+    for (int64_t s0 = 0; s0 < s.BH; s0 += per) {
+        st = run_backward(p, s, s0, std::min<int64_t>(per, s.BH - s0), b, (char*)ws, nullptr, (hipStream_t)stream);
+        if (st != KIA_OK) return st;
+    }
+    return KIA_OK;
 }
 
 size_t kia_geometry_bytes(int B, int H, int T) {
@@ -315,10 +428,11 @@ const char* kia_status_str(kia_status s) {
         case KIA_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
         case KIA_ERR_BUFFER: return "stats or workspace buffer too small";
         case KIA_ERR_HIP: return "HIP launch failed";
+        case KIA_ERR_SCRATCH: return "one (batch, head) slice needs more workspace than kia_backward_noalloc's scratch holds";
     }
     return "unknown status";
 }
 
-int32_t kia_abi_version(void) { return 3; }
+int32_t kia_abi_version(void) { return 4; }
 
 }  // extern "C"

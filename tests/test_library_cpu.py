@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), f"libkia.so does not export {name}"
         assert name in mod.SIGNATURES, f"binding has no signature for {name}"
     assert set(mod.SIGNATURES) == set(names)
-    assert lib.kia_abi_version() == 3
+    assert lib.kia_abi_version() == 4
 
 
 def _params(mod, K=4, tau=6.0, cal=0, rec=0, ste=0, rule=0):
@@ -185,7 +185,7 @@ def test_geometry_probe_size_and_argument_checks():
 
 def test_status_strings():
     lib, _ = _lib()
-    for s in range(7):
+    for s in range(8):
         assert lib.kia_status_str(s)
     assert b"unknown" in lib.kia_status_str(99)
 
@@ -196,3 +196,32 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(mod, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         mod.load()
+
+
+def test_noalloc_backward_argument_checks():
+    """kia_backward_noalloc validates like kia_backward and refuses, before any
+    launch, a shape whose single slice needs more workspace than its scratch
+    (T = 8192: 32,896 tiles of P and dS, 270 MB > 256 MiB)."""
+    lib, mod = _lib()
+    p = _params(mod)
+    B, H, T, d = 2, 3, 100, 64
+    nbytes = lib.kia_stats_bytes(p, B, H, T, d)
+
+    def call(p=p, ptrs=None, sb=nbytes, T=T, d=d):
+        q, k, v, o, do, st, dq, dk, dv = ptrs or [A] * 9
+        return lib.kia_backward_noalloc(p, B, H, T, d, q, k, v, o, do, st, sb, dq, dk, dv, None)
+
+    assert call(p=None) == 1
+    for i in range(9):
+        bad = [A] * 9
+        bad[i] = 0
+        assert call(ptrs=bad) == 1
+        bad[i] = A + 8
+        assert call(ptrs=bad) == 4
+    assert call(sb=nbytes - 1) == 5
+    assert call(d=96) == 2 and call(T=0) == 2
+    assert call(p=_params(mod, cal=1, tau=0.0)) == 3
+    big = lib.kia_stats_bytes(p, B, H, 8192, d)
+    assert call(sb=big, T=8192) == 7
+    assert lib.kia_workspace_bytes(p, 1, 1, 8192, d) > 256 << 20
+    assert lib.kia_workspace_bytes(p, 1, 1, 4096, d) <= 256 << 20
