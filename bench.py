@@ -16,9 +16,21 @@ algorithmic flops per launch over its mean duration is the roofline figure
 from the committed rocprofv3 counter summary when that summary was made from
 the current kernel sources, else reported as null.
 
+Before the W warm-up steps the same step runs for --spinup-ms of wall time
+(default 300 ms, untimed): the GPU's power management needs about 20 ms of
+sustained load to bring its clocks to the steady state a training run sees,
+which the first ~25 steps at this shape do not reach.  The JSON line reports
+the spin-up, the mean step time over the K timed steps (the throughput) and
+the median step and kernel times.
+
 The CPU baseline times the fp64 oracle (tests' reference, not tuned) on a
 bounded sample of the same workload: a fixed number of (b, h) slices, one
-process per host core.
+process per host core up to 16 (the CPU share of one GPU on the GPU hosts),
+with the host's CPU model stated.
+
+The measured fp32 matrix-core peak (libkia_peak.so: independent MFMA chains,
+no memory traffic) is reported beside the spec peak, with the shader clock it
+ran at.
 """
 from __future__ import annotations
 
@@ -131,12 +143,27 @@ def _pool_init():
         os.environ[var] = "1"
 
 
+MAX_CPU_WORKERS = 16   # the host CPU share of one GPU on the GPU hosts
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(wname, variant, n_slices, flop_per_slice):
     import multiprocessing as mp
     from workloads import WORKLOADS
     w = WORKLOADS[wname]
     n_slices = max(1, min(n_slices, w.B * w.H))
-    cores = max(1, min(len(os.sched_getaffinity(0)), 16, n_slices))
+    host_cores = len(os.sched_getaffinity(0))
+    cores = max(1, min(host_cores, MAX_CPU_WORKERS, n_slices))
     slices = [(wname, variant, i // w.H % w.B, i % w.H) for i in range(n_slices)]
     for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
         os.environ[var] = "1"
@@ -151,10 +178,46 @@ def cpu_baseline(wname, variant, n_slices, flop_per_slice):
         "unit": "TFLOP/s",
         "cores": cores,
         "kind": "oracle",
+        "cpu_model": cpu_model(),
+        "host_cores": host_cores,
         "sample": (f"{n_slices} of {w.B * w.H} (b, h) slices of {wname} "
-                   f"(T={w.T}, d={w.d}), fp64 numpy forward+backward, one process per core; "
+                   f"(T={w.T}, d={w.d}), fp64 numpy forward+backward, one process per core on {cores} of the "
+                   f"host's {host_cores} cores (at most {MAX_CPU_WORKERS}, the CPU share of one GPU); "
                    f"{sum(per):.1f} s of CPU work in {wall:.1f} s wall"),
     }
+
+
+def mfma_peak(dev_index=0, grid=2048, iters=200, repeats=3):
+    """fp32 matrix-core throughput of libkia_peak.so's register-only MFMA
+    chains (best of a few launches) and the median shader clock of its
+    waves (s_memtime cycles over s_memrealtime's 100 MHz ticks)."""
+    import numpy as np
+    import torch
+    path = os.path.join(ROOT, "quantized_softmax_attention_amd", "libkia_peak.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.kia_peak_mfma_f32.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    dev = torch.device("cuda", dev_index)
+    out = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+    clk = torch.zeros(2 * grid, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    best, ghz = 0.0, float("nan")
+    flop = grid * 4 * 16 * iters * 4096          # 4 waves per workgroup, 16 MFMAs per iteration
+    for _ in range(repeats):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        if lib.kia_peak_mfma_f32(out.data_ptr(), clk.data_ptr(), iters, grid, stream) != 0:
+            return None
+        b.record()
+        torch.cuda.synchronize()
+        tf = flop / (a.elapsed_time(b) * 1e-3) / 1e12
+        if tf > best:
+            c = clk.cpu().numpy().reshape(grid, 2).astype(np.float64)
+            best, ghz = tf, float(np.median(c[:, 0] / (c[:, 1] / 1e8)) / 1e9)
+    return {"tflops": round(best, 2), "clock_ghz": round(ghz, 3), "frac_of_spec": round(best / PEAK_FP32_MFMA, 4),
+            "probe": "register-only v_mfma_f32_32x32x2_f32 chains, 4 waves per workgroup, "
+                     f"{grid} workgroups (libkia_peak.so)"}
 
 
 def _find_csv(d, suffix):
@@ -259,6 +322,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--spinup-ms", type=float, default=300.0,
+                    help="untimed wall time of steps before the warm-up steps (power-management ramp)")
     ap.add_argument("--workload", default="c2", choices=sorted(DEFAULT_VARIANT))
     ap.add_argument("--K", type=int)
     ap.add_argument("--calibration", choices=["minmax", "fwm", "fwm_untrunc"])
@@ -269,6 +334,7 @@ def main():
                     help="oracle sample size for the CPU baseline, in (b, h) slices (capped at B*H)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true", help="skip timing the geometry probe")
+    ap.add_argument("--no-peak", action="store_true", help="skip the measured matrix-core peak")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--ingest-pmc", metavar="DIR",
@@ -343,6 +409,15 @@ def main():
         kia.kia_forward(tq, tk, tv, params, o=o, stats=stats, events=evf)
         kia.kia_backward(tq, tk, tv, o, tdo, stats, params, dq=dq, dk=dk, dv=dv, ws=ws, events=evb)
 
+    # spin-up: the same step, untimed, until the clocks have settled
+    spin_steps = 0
+    t_spin = time.perf_counter()
+    while (time.perf_counter() - t_spin) * 1e3 < args.spinup_ms:
+        for _ in range(20):
+            step()
+        spin_steps += 20
+        torch.cuda.synchronize()
+    spin_ms = (time.perf_counter() - t_spin) * 1e3
     for _ in range(args.warmup):
         step()
     ev = HipEvents()
@@ -356,12 +431,18 @@ def main():
     ms_step = wall_ms / args.steps
 
     per_kernel = {name: [] for name in KERNELS}
+    per_step = []
     for evf, evb in evs:
         per_kernel["forward"].append(ev.ms(evf[0], evf[1]))
         per_kernel["backward_rows"].append(ev.ms(evb[0], evb[1]))
         per_kernel["backward_cols"].append(ev.ms(evb[2], evb[3]))
+        per_step.append(ev.ms(evf[0], evb[3]))
     ev.close()
     kern_ms = {name: float(np.mean(vals)) for name, vals in per_kernel.items()}
+    kern_median = {name: float(np.median(vals)) for name, vals in per_kernel.items()}
+    step_median = float(np.median(per_step))
+
+    peak = None if args.no_peak else mfma_peak()
     dominant = max(("forward", "backward_rows", "backward_cols"), key=lambda n: kern_ms[n])
     achieved = flop_kernel / (kern_ms[dominant] * 1e-3) / 1e12
 
@@ -432,7 +513,12 @@ def main():
                      "kernel": dominant, "flop_per_launch": flop_kernel,
                      "avg_ms": round(kern_ms[dominant], 4)},
         "kernel_ms": {n: round(t, 4) for n, t in kern_ms.items()},
+        "kernel_ms_median": {n: round(t, 4) for n, t in kern_median.items()},
+        "ms_per_step_median": round(step_median, 4),
+        "spinup": {"ms": round(spin_ms, 1), "steps": spin_steps},
     }
+    if peak is not None:
+        out["mfma_peak_measured"] = peak
     if probe is not None:
         out["geometry_probe"] = probe
     if cpu is not None:
