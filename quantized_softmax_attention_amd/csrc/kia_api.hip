@@ -118,6 +118,7 @@ kia::FwdConfig config_of(const kia_params* p, int d, bool dump) {
     c.rec = p->reconstruction;
     c.prob = prob_extras(p);
     c.dump = dump;
+    c.tab = kia::tab_capable(c.cal, c.rec) && p->n_intervals <= kia::kTabMaxK;
     return c;
 }
 

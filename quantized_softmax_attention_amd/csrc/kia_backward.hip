@@ -38,16 +38,15 @@
 
 namespace kia {
 
-template <int D, int CAL, int REC, bool PROB>
+template <int D, int CAL, int REC, bool PROB, bool TAB>
 __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows_kernel(BwdArgs a) {
     constexpr int NB = D / 32;
     using LT = LdsTile<D>;
     constexpr int BUF = 2 * LT::kFloats;    // V tile, then K tile
     constexpr int XS = 36;                  // row stride of the per-wave transpose scratch
-    constexpr int NSTAGE = 2 * (D / 32);     // direct LDS loads per wave for one staged V + K pair
     __shared__ __attribute__((aligned(16))) float lds[2 * BUF];
     __shared__ __attribute__((aligned(16))) float xpose[kWaves * kTile * XS];
-    __shared__ __attribute__((aligned(16))) float sbuf[kWaves * kTileElems];  // each wave's next score tile
+    __shared__ float gtab[TAB ? kWaves * kTabWaveFloats : 1];  // each wave's grid table
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
@@ -71,7 +70,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
     float* ptiles = a.probs + tile0;
     float* dstiles = a.dscores + tile0;
     float* xw = xpose + wave * kTile * XS;
-    float* sw = sbuf + wave * kTileElems;
+    float* gt = gtab + (TAB ? wave * kTabWaveFloats : 0);
 
     // B operand of dP^T = V dO^T (dO row of this lane's query), and delta.
     const float* oe = (REC == REC_NEAREST && PROB) ? a.o_lerp : a.o;
@@ -105,6 +104,24 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
     const float lw = qvalid ? __log2f(invW) : -INFINITY;
     const float nd = -dlt * invWe;               // G = (dP * invWe + nd) * g
     const float gW = invWe * W, ndW = nd * W;    // the same with g / W folded into gw
+    // c/h is folded into the grid factor, so the loop forms dS = G c/h in one
+    // product; the row sums are accumulated in units of dS and 1/coh restores
+    // G's units after the loop
+    const float lc = __log2f(rg.coh);            // log2(c/h)
+    const float lwc = lw + lc;                   // log2(c/(h W))
+    const float icoh = 1.f / rg.coh, cicoh = rg.c * icoh;
+    const float iwc = fast_exp2(lw - lc);        // 1/(W c/h): Nearest's hard P from its table entry
+    if (TAB) {
+        // the row's grid factors for indices 0..K: g_i c/(h W) under LERP,
+        // g_i c/h under Nearest; the two lane halves fill alternate entries
+#pragma unroll
+        for (int j = 0; j < (kTabEntries + 1) / 2; ++j) {
+            const int i = 2 * j + hl;
+            if (i <= a.K) gt[tab_off(i, li)] = fast_exp2(fmaf(-(float)i, rg.hl2, REC == REC_LERP ? lwc : lc));
+        }
+        wait_lgkm0();
+        __builtin_amdgcn_wave_barrier();
+    }
 
     // Row sums of the direct term (SA) and of dL/dw * Wd (SB = (c/h - 1) SBu + c SBf).
     // SA is summed per tile in fp32 (in key order, no contraction, so the
@@ -120,7 +137,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
 
     LT::load(lds, V, 0, T, tid);
     LT::load(lds + LT::kFloats, Kp, 0, T, tid);
-    if (active) dma_tile(sw, stiles, lane);
     wait_vmcnt<0>();
     __syncthreads();
 
@@ -128,29 +144,22 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
     for (int kt = 0; kt <= kt_end; ++kt) {
         const float* vcur = lds + (kt & 1) * BUF;
         const float* kcur = vcur + LT::kFloats;
+        const bool work = active && kt <= qt;
         if (kt < kt_end) {
             float* nxt = lds + ((kt + 1) & 1) * BUF;
             LT::load(nxt, V, (kt + 1) * kTile, T, tid);
             LT::load(nxt + LT::kFloats, Kp, (kt + 1) * kTile, T, tid);
         }
-        const bool work = active && kt <= qt;
-        const bool prefetch = active && kt < qt;
+        // this tile's scores straight into registers, after the staging loads;
+        // they are first needed after the dP products
+        f32x4 sx[4];
+        if (work) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                sx[p] = __builtin_nontemporal_load((const f32x4*)(stiles + (size_t)kt * kTileElems + p * 256 + lane * 4));
+        }
         if (work) {
             const int k0 = kt * kTile;
-            // scores of this tile: direct-loaded during the previous tile, before
-            // its 8 P / dS stores and this tile's staging loads
-            if (kt == 0) {
-                if (kt < kt_end) wait_vmcnt<NSTAGE>();
-                else wait_vmcnt<0>();
-            } else {
-                if (kt < kt_end) wait_vmcnt<NSTAGE + 8>();
-                else wait_vmcnt<8>();
-            }
-            read_tile(sw, lane, scur);
-            if (prefetch) {
-                wait_lgkm0();
-                dma_tile(sw, stiles + (size_t)(kt + 1) * kTileElems, lane);
-            }
             f32x4 xv[D / 8];
 #pragma unroll
             for (int p = 0; p < D / 8; ++p) xv[p] = *(const f32x4*)(vcur + LT::off(li, 8 * p + 4 * hl));
@@ -162,6 +171,13 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
             float xk[16 * NB];
 #pragma unroll
             for (int s2 = 0; s2 < 16 * NB; ++s2) xk[s2] = kcur[LT::off(acc_row(s2 & 15, hl), 32 * (s2 >> 4) + li)];
+            // nothing that reads the scores moves above this point (their loads
+            // may still be in flight during the products)
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) scur[4 * p + j] = sx[p][j];
 
             float ds[16], pr[16];
             auto grads = [&](auto diag_t) {
@@ -194,23 +210,35 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
                     const float f = u - fi;
                     // G = dL/dw times the LERP segment's grid value g_i; the direct
                     // term and the h-derivative share it
-                    float G, pw;
+                    // dS = G c/h with G = dL/dw times the LERP segment's grid value
+                    // g_i; the direct term and the h-derivative share it
+                    float Gc, pw;
                     if (REC == REC_LERP) {
-                        // gw = g_i / W in one exponential; P = gw (1 - f c)
-                        const float gw = fast_exp2(fmaf(-fi, rg.hl2, lw));
-                        pw = gw * fmaf(-f, rg.c, 1.f);
-                        G = fmaf(dp[r], gW, ndW) * gw;
+                        // gwc = g_i c/(h W) from one table entry or exponential;
+                        // P = g_i (1 - f c) / W = gwc (1 - f c) h/c
+                        const float gwc = TAB ? gt[tab_off((int)fi, li)] : fast_exp2(fmaf(-fi, rg.hl2, lwc));
+                        pw = gwc * fmaf(-f, cicoh, icoh);
+                        Gc = fmaf(dp[r], gW, ndW) * gwc;
                     } else {
-                        const float g = fast_exp2(-fi * rg.hl2);
-                        pw = fast_exp2(fmaf(-floorf(u + 0.5f), rg.hl2, lw));
-                        G = fmaf(dp[r], invWe, nd) * g;
+                        const float rn = floorf(u + 0.5f);
+                        float gc;
+                        if constexpr (TAB) {
+                            gc = gt[tab_off((int)fi, li)];
+                            // the hard weight's grid point (past K only outside the FWM window)
+                            pw = gt[tab_off((int)((CAL == CAL_FWM) ? fminf(rn, rg.Kf) : rn), li)] * iwc;
+                        } else {
+                            gc = fast_exp2(fmaf(-fi, rg.hl2, lc));
+                            pw = fast_exp2(fmaf(-rn, rg.hl2, lw));
+                        }
+                        Gc = fmaf(dp[r], invWe, nd) * gc;
                     }
                     pr[r] = keep ? pw : 0.f;
-                    ds[r] = keep ? G * rg.coh : 0.f;
+                    ds[r] = keep ? Gc : 0.f;
                     SA += ds[r];
                     if (CAL == CAL_MINMAX) {
-                        // dL/dw * Wd with Wd / g = (c/h - 1) u + c f (i + 1); only h = span/K needs it
-                        const float Gk = keep ? G : 0.f;
+                        // dL/dw * Wd with Wd / g = (c/h - 1) u + c f (i + 1); only h = span/K
+                        // needs it (in units of dS: divided by c/h after the loop)
+                        const float Gk = ds[r];
                         SBu = fmaf(Gk, u, SBu);
                         SBf = fmaf(Gk, fmaf(f, fi, f), SBf);
                     }
@@ -252,20 +280,16 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
                 SA = 0.f;
             }
         }
-        // the staging loads were issued first; the score prefetch (4) and the
-        // P / dS stores (8) may stay in flight
-        if (work) {
-            if (prefetch) wait_vmcnt<12>();
-            else wait_vmcnt<8>();
-        } else {
-            wait_vmcnt<0>();
-        }
+        // the staging loads were issued before the scores (already consumed) and
+        // the P / dS stores (8), which may stay in flight
+        if (work) wait_vmcnt<8>();
+        else wait_vmcnt<0>();
         lds_barrier();
     }
 
     SBu += __shfl_xor(SBu, 32);
     SBf += __shfl_xor(SBf, 32);
-    const float SB = rg.cohm1 * SBu + rg.c * SBf;
+    const float SB = (rg.cohm1 * SBu + rg.c * SBf) * icoh;
     const bool p1 = a.rule == GRAD_P1;
     const bool use_max = !rg.degen && (a.rule == GRAD_FULL || a.rule == GRAD_MAX_ONLY);
     const bool use_min = !rg.degen && CAL == CAL_MINMAX && (a.rule == GRAD_FULL || a.rule == GRAD_MIN_ONLY);
@@ -446,12 +470,21 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_cols
     }
 }
 
-template <int D, int CAL, int REC, bool PROB>
+template <int D, int CAL, int REC, bool PROB, bool TAB = false>
 static hipError_t launch_rows_t(const BwdArgs& a, hipStream_t s) {
     const int n_blk = (a.n_t + kBlockTiles - 1) / kBlockTiles;
-    hipLaunchKernelGGL((kia_backward_rows_kernel<D, CAL, REC, PROB>), dim3((unsigned)(a.BH * n_blk)),
+    hipLaunchKernelGGL((kia_backward_rows_kernel<D, CAL, REC, PROB, TAB>), dim3((unsigned)(a.BH * n_blk)),
                        dim3(kThreads), 0, s, a);
     return hipGetLastError();
+}
+
+// Grid operators: the table instantiation when the row's grid fits the table.
+template <int D, int CAL, int REC, bool PROB>
+static hipError_t launch_rows_grid(const FwdConfig& c, const BwdArgs& a, hipStream_t s) {
+    if constexpr (tab_capable(CAL, REC)) {
+        if (c.tab) return launch_rows_t<D, CAL, REC, PROB, true>(a, s);
+    }
+    return launch_rows_t<D, CAL, REC, PROB>(a, s);
 }
 
 template <int D, int CAL>
@@ -464,9 +497,9 @@ static hipError_t launch_rows_rec(const FwdConfig& c, const BwdArgs& a, hipStrea
         }
         return hipErrorInvalidValue;
     }
-    if (c.rec == REC_LERP) return launch_rows_t<D, CAL, REC_LERP, false>(a, s);
-    return c.prob ? launch_rows_t<D, CAL, REC_NEAREST, true>(a, s)
-                  : launch_rows_t<D, CAL, REC_NEAREST, false>(a, s);
+    if (c.rec == REC_LERP) return launch_rows_grid<D, CAL, REC_LERP, false>(c, a, s);
+    return c.prob ? launch_rows_grid<D, CAL, REC_NEAREST, true>(c, a, s)
+                  : launch_rows_grid<D, CAL, REC_NEAREST, false>(c, a, s);
 }
 
 template <int D>

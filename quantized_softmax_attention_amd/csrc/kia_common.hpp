@@ -72,78 +72,6 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kBlockTiles = kWaves;  // stationary 32-row tiles per workgroup
 
-// LDS layouts of a streamed 32 x D tile (rows r of a row-major [T][D] tensor):
-//  row-major  rm(r, c) = r*(D+4) + c: lane = row, float4 along c (no conflicts)
-//  transposed tr(c, r) = c*32 + 4*((r/4) ^ ((c/2)%8)) + r%4: lane = column
-//             c, float4 along 4 consecutive rows.  With 64 banks a column of
-//             32 floats covers one bank half (c even / odd); the xor on c/2
-//             gives the 8 columns of each half that one float4 read phase
-//             touches 8 distinct 4-bank groups.
-template <int D>
-__device__ __forceinline__ int rm_off(int r, int c) { return r * (D + 4) + c; }
-__device__ __forceinline__ int tr_off(int c, int r) {
-    return c * kTile + 4 * ((r >> 2) ^ ((c >> 1) & 7)) + (r & 3);
-}
-
-template <int D>
-struct StreamTile {
-    static constexpr int kF4 = kTile * D / 4 / kThreads;  // float4 per thread
-    static constexpr int kRM = kTile * (D + 4);          // floats of a row-major staged tile
-    static constexpr int kTR = D * kTile;                // floats of a transposed staged tile
-    f32x4 v[kF4];
-
-    // row-major staging: consecutive threads read consecutive float4 of a row.
-    // Rows at or past T read as zero; full tiles (the uniform common case) skip the test.
-    __device__ __forceinline__ void load_rm(const float* src, int r0, int T, int tid) {
-        if (r0 + kTile <= T) {
-#pragma unroll
-            for (int i = 0; i < kF4; ++i) {
-                const int e = tid + kThreads * i, r = e / (D / 4), c4 = e % (D / 4);
-                v[i] = *(const f32x4*)(src + (size_t)(r0 + r) * D + 4 * c4);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < kF4; ++i) {
-                const int e = tid + kThreads * i, r = e / (D / 4), c4 = e % (D / 4);
-                v[i] = (r0 + r < T) ? *(const f32x4*)(src + (size_t)(r0 + r) * D + 4 * c4)
-                                    : f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-        }
-    }
-    __device__ __forceinline__ void store_rm(float* lds, int tid) const {
-#pragma unroll
-        for (int i = 0; i < kF4; ++i) {
-            const int e = tid + kThreads * i, r = e / (D / 4), c4 = e % (D / 4);
-            *(f32x4*)(lds + rm_off<D>(r, 4 * c4)) = v[i];
-        }
-    }
-    // transposed staging: a wave's lanes take 32 consecutive rows of one float4 column
-    __device__ __forceinline__ void load_tr(const float* src, int r0, int T, int tid) {
-        if (r0 + kTile <= T) {
-#pragma unroll
-            for (int i = 0; i < kF4; ++i) {
-                const int e = tid + kThreads * i, r = e & 31, c4 = e >> 5;
-                v[i] = *(const f32x4*)(src + (size_t)(r0 + r) * D + 4 * c4);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < kF4; ++i) {
-                const int e = tid + kThreads * i, r = e & 31, c4 = e >> 5;
-                v[i] = (r0 + r < T) ? *(const f32x4*)(src + (size_t)(r0 + r) * D + 4 * c4)
-                                    : f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-        }
-    }
-    __device__ __forceinline__ void store_tr(float* lds, int tid) const {
-#pragma unroll
-        for (int i = 0; i < kF4; ++i) {
-            const int e = tid + kThreads * i, r = e & 31, c4 = e >> 5;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) lds[tr_off(4 * c4 + j, r)] = v[i][j];
-        }
-    }
-};
-
 // A 32 x D tile of a row-major [T][D] tensor staged in LDS by the whole
 // workgroup with direct global -> LDS loads (global_load_lds_dwordx4: each
 // lane's 16 bytes land at slot lane of a 1 KB chunk, no registers involved).
@@ -193,12 +121,12 @@ struct LdsTile {
 };
 
 // Direct global -> LDS copy of one wave's 4 KB fragment-native tile (the
-// score, probability and score-gradient tiles): lane l fetches its float4 of
-// each 1 KB chunk, which lands at the same place in the wave's LDS slot, so
-// the lane later reads back exactly the registers it would have loaded.
-// Each such tile is read once per kernel, so the loads are non-temporal
-// (cache policy NT): they do not displace the K, V, Q, dO tiles that every
-// workgroup of a slice re-reads from L2.
+// column kernel's probability and score-gradient tiles): lane l fetches its
+// float4 of each 1 KB chunk, which lands at the same place in the wave's LDS
+// slot, so the lane later reads back exactly the registers it would have
+// loaded.  Each such tile is read once per kernel, so the loads are
+// non-temporal (cache policy NT): they do not displace the Q and dO tiles
+// that every workgroup of a slice re-reads from L2.
 constexpr int kCpolNonTemporal = 2;
 __device__ __forceinline__ void dma_tile(float* lds_wave, const float* src, int lane) {
 #pragma unroll
@@ -226,8 +154,14 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Wait until at most N vector memory operations of this wave are outstanding
-// (lgkm and exp counters left free).  Vector memory operations complete in
-// issue order, so this waits for everything issued before the last N.
+// (lgkm and exp counters left free).  On this architecture vector memory
+// operations (loads, stores, global -> LDS loads) report completion to the
+// wave in execution order; the one exception LLVM's AMDGPU memory model
+// documents for GFX90A / GFX942 is a FLAT instruction that touches LDS, and
+// these kernels issue only global_* instructions.  (The compiler's own wait
+// insertion relies on the same ordering: it waits for a load by counting the
+// vector memory operations issued after it, loads and stores alike.)  So
+// this waits for everything issued before the last N.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -345,6 +279,25 @@ __device__ __forceinline__ RowGrid make_row_grid(float m, float n, int K, float 
     }
     g.cohm1 = g.coh - 1.f;
     return g;
+}
+
+// Grid table: for rows whose grid has at most kTabMaxK intervals, the K+1
+// values of the row's grid (scaled as the kernel needs them) are computed once
+// per row block and kept in LDS, and each score's reconstruction reads its
+// segment's or grid point's value instead of evaluating an exponential.  Each
+// wave holds the table of its 32 rows, column-major: entry i of row li at
+// i*32 + li, so the lanes of different rows read different banks whatever
+// index they take (only the two lane halves of one row can collide).
+constexpr int kTabMaxK = 32;
+constexpr int kTabEntries = kTabMaxK + 1;
+constexpr int kTabWaveFloats = kTabEntries * kTile;
+__device__ __forceinline__ int tab_off(int i, int li) { return i * kTile + li; }
+
+// Whether a (calibration, reconstruction) pair reads its grid values from the
+// table: the finite grids (MinMax, FWM) under LERP and Nearest.  The
+// untruncated step's grid is unbounded and the softmax family has none.
+constexpr bool tab_capable(int cal, int rec) {
+    return (cal == CAL_MINMAX || cal == CAL_FWM) && (rec == REC_LERP || rec == REC_NEAREST);
 }
 
 // exp2 on the hardware transcendental unit.  Results below the fp32 normal

@@ -26,7 +26,6 @@ template <int D, int CAL, int REC, bool PROB, bool DUMP>
 __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forward_kernel(FwdArgs a) {
     static_assert(D % 32 == 0, "head dim must be a multiple of 32");
     constexpr int NB = D / 32;  // 32-wide blocks of the head dim
-    constexpr int NSTAGE = D / 32;  // direct LDS loads per wave for one staged tile
     using LT = LdsTile<D>;
     constexpr int BUF = LT::kFloats;
     // K (sweep 1) / V (sweep 2) tiles, double-buffered.  The two buffers are
@@ -35,7 +34,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
     // from reads of the other and inserts no wait of its own between them.
     __shared__ __attribute__((aligned(16))) float lds0[BUF];
     __shared__ __attribute__((aligned(16))) float lds1[BUF];
-    __shared__ __attribute__((aligned(16))) float sbuf[kWaves * kTileElems];  // each wave's next score tile
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index is uniform
@@ -56,7 +54,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
     const float* V = a.v + head;
     const int64_t tiles_per_head = (int64_t)n_t * (n_t + 1) / 2;
     float* tiles = a.tiles + ((size_t)bh * tiles_per_head + (active ? tile_index(qt, 0) : 0)) * kTileElems;
-    float* sw = sbuf + wave * kTileElems;
 
     // B operand of S^T = K Q^T: lane holds Q[qrow][c] / sqrt(d) for c = 8p + 4*hl + j.
     float qf[D / 2];
@@ -257,6 +254,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
         }
     };
 
+    // Score tiles go straight into registers, loaded one tile ahead of their
+    // reconstruction (sx), which itself runs one tile ahead of the products.
+    f32x4 sx[4];
     LT::load(lds0, V, 0, T, tid);
     if (active) {
 #pragma unroll
@@ -265,7 +265,11 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
 #pragma unroll
             for (int j = 0; j < 4; ++j) sv[4 * p + j] = x[j];
         }
-        if (qt > 0) dma_tile(sw, tiles + kTileElems, lane);
+        if (qt > 0) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                sx[p] = __builtin_nontemporal_load((const f32x4*)(tiles + kTileElems + p * 256 + lane * 4));
+        }
         if (qt == 0) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) recon(0, std::true_type{}, r, wA, wlA);
@@ -280,20 +284,27 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
     // tile kt: weights in (w, wl); reconstruct tile kt+1 into (wn, wln)
     auto sweep2 = [&](int kt, const float* cur, float* nxt, const float* w, const float* wl, float* wn, float* wln)
         __attribute__((always_inline)) {
-        if (kt < kt_end) LT::load(nxt, V, (kt + 1) * kTile, T, tid);
         const bool more = active && kt + 1 <= qt;      // tile kt+1 exists for this wave
         const bool prefetch = active && kt + 2 <= qt;  // and tile kt+2
+        if (more) {
+            // scores of tile kt+1, loaded during the previous tile: the only
+            // vector memory operations of this wave still outstanding here
+            wait_vmcnt<0>();
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sv[4 * p + j] = sx[p][j];
+        }
+        if (kt < kt_end) LT::load(nxt, V, (kt + 1) * kTile, T, tid);
+        if (prefetch) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                sx[p] = __builtin_nontemporal_load(
+                    (const f32x4*)(tiles + (size_t)(kt + 2) * kTileElems + p * 256 + lane * 4));
+        }
+        // the score loads are issued here, ahead of this tile's work
+        __builtin_amdgcn_sched_barrier(0);
         if (active && kt <= qt) {
-            if (more) {
-                // scores of tile kt+1 (direct-loaded during the previous tile)
-                if (kt < kt_end) wait_vmcnt<NSTAGE>();
-                else wait_vmcnt<0>();
-                read_tile(sw, lane, sv);
-                if (prefetch) {
-                    wait_lgkm0();
-                    dma_tile(sw, tiles + (size_t)(kt + 2) * kTileElems, lane);
-                }
-            }
             // V^T operand: lane = head-dim column, one float per key (column reads)
             float xv[16 * NB];
 #pragma unroll
@@ -315,7 +326,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
             }
         }
         flush_sums();
-        // the V tile loads were issued first; the score prefetch may stay in flight
+        // the V tile loads were issued before the 4 score loads, which may stay in flight
         if (prefetch) wait_vmcnt<4>();
         else wait_vmcnt<0>();
         lds_barrier();
@@ -373,6 +384,11 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int D, int CAL, int REC, bool PROB>
+static hipError_t launch_fwd_grid(const FwdConfig& c, const FwdArgs& a, hipStream_t s) {
+    return c.dump ? launch_fwd_t<D, CAL, REC, PROB, true>(a, s) : launch_fwd_t<D, CAL, REC, PROB, false>(a, s);
+}
+
 template <int D, int CAL>
 static hipError_t launch_fwd_rec(const FwdConfig& c, const FwdArgs& a, hipStream_t s) {
     if (softmax_rec(c.rec)) {
@@ -389,14 +405,9 @@ static hipError_t launch_fwd_rec(const FwdConfig& c, const FwdArgs& a, hipStream
         }
         return hipErrorInvalidValue;
     }
-    if (c.rec == REC_LERP)
-        return c.dump ? launch_fwd_t<D, CAL, REC_LERP, false, true>(a, s)
-                      : launch_fwd_t<D, CAL, REC_LERP, false, false>(a, s);
-    if (c.prob)
-        return c.dump ? launch_fwd_t<D, CAL, REC_NEAREST, true, true>(a, s)
-                      : launch_fwd_t<D, CAL, REC_NEAREST, true, false>(a, s);
-    return c.dump ? launch_fwd_t<D, CAL, REC_NEAREST, false, true>(a, s)
-                  : launch_fwd_t<D, CAL, REC_NEAREST, false, false>(a, s);
+    if (c.rec == REC_LERP) return launch_fwd_grid<D, CAL, REC_LERP, false>(c, a, s);
+    if (c.prob) return launch_fwd_grid<D, CAL, REC_NEAREST, true>(c, a, s);
+    return launch_fwd_grid<D, CAL, REC_NEAREST, false>(c, a, s);
 }
 
 template <int D>

@@ -66,6 +66,7 @@ struct GeoArgs {
 struct FwdConfig {
     int d, cal, rec;
     bool prob, dump;
+    bool tab;  // grid values from the per-row LDS table (K <= kTabMaxK, finite grid)
 };
 
 hipError_t launch_forward(const FwdConfig& c, const FwdArgs& a, hipStream_t s);
