@@ -72,6 +72,11 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
     float* xw = xpose + wave * kTile * XS;
     float* gt = gtab + (TAB ? wave * kTabWaveFloats : 0);
 
+    // The first V and K tiles go out first, so their loads overlap those of
+    // the row's operands and statistics below.
+    LT::load(lds, V, 0, T, tid);
+    LT::load(lds + LT::kFloats, Kp, 0, T, tid);
+
     // B operand of dP^T = V dO^T (dO row of this lane's query), and delta.
     const float* oe = (REC == REC_NEAREST && PROB) ? a.o_lerp : a.o;
     float dof[D / 2];
@@ -96,6 +101,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
     const float n = qvalid ? a.row_n[ri] : 0.f;
     const float W = qvalid ? a.row_w[ri] : 1.f;
     const float WL = qvalid ? a.row_wl[ri] : 1.f;
+    // causal key indices by construction; clamped so no stats value can address outside the row
+    const int ka = min(max(qvalid ? a.row_a[ri] : 0, 0), max(qrow, 0));
+    const int kb = min(max(qvalid ? a.row_b[ri] : 0, 0), max(qrow, 0));
     const RowGrid rg = make_row_grid(m, n, a.K, a.tau, CAL);
     const float invW = 1.f / W;
     // a row with a single causal key has P = 1 whatever its score: zero gradient
@@ -135,8 +143,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
 #pragma unroll
     for (int b = 0; b < NB; ++b) dq[b] = f32x16{};
 
-    LT::load(lds, V, 0, T, tid);
-    LT::load(lds + LT::kFloats, Kp, 0, T, tid);
     wait_vmcnt<0>();
     __syncthreads();
 
@@ -293,12 +299,42 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
     const bool p1 = a.rule == GRAD_P1;
     const bool use_max = !rg.degen && (a.rule == GRAD_FULL || a.rule == GRAD_MAX_ONLY);
     const bool use_min = !rg.degen && CAL == CAL_MINMAX && (a.rule == GRAD_FULL || a.rule == GRAD_MIN_ONLY);
-    // causal key indices by construction; clamped so no stats value can address outside the row
-    const int ka = min(max(qvalid ? a.row_a[ri] : 0, 0), max(qrow, 0));
-    const int kb = min(max(qvalid ? a.row_b[ri] : 0, 0), max(qrow, 0));
 
     // the wave's dS tile stores must be visible before it reads and updates them
     __threadfence_block();
+
+    // Every value the epilogue reads depends only on (ka, kb), known since the
+    // prologue: the reads all go out here, before any of them is used.
+    const float* ta = dstiles + (size_t)(ka >> 5) * kTileElems;
+    const int kra = ka & 31;
+    const bool reread = qvalid && use_max && ((kra >> 2) & 1) == hl;
+    float tv[16];
+    if (reread) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tv[r] = ta[kmajor_offset(li, acc_row(r, hl))];
+    }
+    float* ea = dstiles + (size_t)(ka >> 5) * kTileElems + kmajor_offset(li, kra);
+    float* eb = dstiles + (size_t)(kb >> 5) * kTileElems + kmajor_offset(li, kb & 31);
+    float olda = 0.f, oldb = 0.f;
+    if (qvalid && use_max) olda = *ea;
+    if (qvalid && use_min && hl == 0) oldb = *eb;
+    // K rows a(t), b(t) and the P1 prefix row; entry i holds columns 8 i + 4 hl .. + 3
+    f32x4 ra[4 * NB], rb[4 * NB], rp[4 * NB];
+#pragma unroll
+    for (int i = 0; i < 4 * NB; ++i) {
+        ra[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        rb[i] = ra[i];
+        rp[i] = ra[i];
+    }
+    if (qvalid) {
+#pragma unroll
+        for (int i = 0; i < 4 * NB; ++i) {
+            const int c = 8 * i + 4 * hl;
+            ra[i] = *(const f32x4*)(Kp + (size_t)ka * D + c);
+            rb[i] = *(const f32x4*)(Kp + (size_t)kb * D + c);
+            if (p1) rp[i] = *(const f32x4*)(a.prefix_k + head + (size_t)qrow * D + c);
+        }
+    }
 
     // The argmax entry receives C_m = -SA + SB/K (MinMax) or -SA (FWM), so its
     // final value is minus the other keys' direct terms (plus SB/K).  Where P
@@ -306,21 +342,17 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
     // dP - delta, far above the row's true gradient, and adding C_m to it would
     // cancel that noise only to its rounding.  So the final value is formed
     // from the other keys alone: the lane half holding key a re-reads its 16
-    // entries of that tile, reproduces the tile's partial sum bit for bit and
-    // replaces it by the partial without key a.
+    // entries of that tile (tv), reproduces the tile's partial sum bit for bit
+    // and replaces it by the partial without key a.
     // (The noisy partial is taken out of hi first, which is exact, so no
     // intermediate carries its magnitude into the fp64 rounding.)
     double sa_lane = (double)SAhi + (double)SAlo;
-    const float* ta = dstiles + (size_t)(ka >> 5) * kTileElems;
-    const int kra = ka & 31;
-    if (qvalid && use_max && ((kra >> 2) & 1) == hl) {
+    if (reread) {
         float p_all = 0.f, p_ex = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int kk = acc_row(r, hl);
-            const float x = ta[kmajor_offset(li, kk)];
-            p_all += x;
-            p_ex += (kk == kra) ? 0.f : x;
+            p_all += tv[r];
+            p_ex += (acc_row(r, hl) == kra) ? 0.f : tv[r];
         }
         sa_lane = (((double)SAhi - (double)p_all) + (double)SAlo) + (double)p_ex;
     }
@@ -334,36 +366,26 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
     if (qvalid) {
         float cm = 0.f;
         if (use_max) {
-            // both lane halves read the loop's direct term; the first writes the final value
-            float* e = dstiles + (size_t)(ka >> 5) * kTileElems + kmajor_offset(li, kra);
-            const float old = *e;
+            // both lane halves read the loop's direct term (olda); the first writes the final value
             const float fin = (float)(sbk - sa_excl);
-            cm = fin - old;  // the routed C_m, as applied on top of the loop's direct term
-            if (hl == 0) *e = fin;
+            cm = fin - olda;  // the routed C_m, as applied on top of the loop's direct term
+            if (hl == 0) *ea = fin;
         }
         float* dqrow = a.dq + head + (size_t)qrow * D;
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
+        for (int i = 0; i < 4 * NB; ++i) {
+            const int b = i >> 2, p = i & 3;
+            f32x4 y;
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int c = 32 * b + 8 * p + 4 * hl;
-                const f32x4 xa = *(const f32x4*)(Kp + (size_t)ka * D + c);
-                const f32x4 xb = *(const f32x4*)(Kp + (size_t)kb * D + c);
-                f32x4 pk = {0.f, 0.f, 0.f, 0.f};
-                if (p1) pk = *(const f32x4*)(a.prefix_k + head + (size_t)qrow * D + c);
-                f32x4 y;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) y[j] = (dq[b][4 * p + j] + cm * xa[j] + cn * xb[j] - mu * pk[j]) * a.scale;
-                *(f32x4*)(dqrow + c) = y;
-            }
+            for (int j = 0; j < 4; ++j)
+                y[j] = (dq[b][4 * p + j] + cm * ra[i][j] + cn * rb[i][j] - mu * rp[i][j]) * a.scale;
+            *(f32x4*)(dqrow + 8 * i + 4 * hl) = y;
+        }
         if (hl == 0) {
             a.row_cm[ri] = p1 ? mu : cm;
             a.row_cn[ri] = cn;
             // argmax != argmin whenever C_n is routed (non-degenerate rows)
-            if (cn != 0.f) {
-                float* e = dstiles + (size_t)(kb >> 5) * kTileElems + kmajor_offset(li, kb & 31);
-                *e += cn;
-            }
+            if (cn != 0.f) *eb = oldb + cn;
         }
     }
 }

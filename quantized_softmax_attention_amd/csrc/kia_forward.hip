@@ -23,9 +23,14 @@
 namespace kia {
 
 template <int D, int CAL, int REC, bool PROB, bool DUMP>
-__global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forward_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_forward_kernel(FwdArgs a) {
     static_assert(D % 32 == 0, "head dim must be a multiple of 32");
     constexpr int NB = D / 32;  // 32-wide blocks of the head dim
+    // Sweep 2 reconstructs one tile ahead of the products (PIPE) unless the
+    // Prob-STE extras at d = 64 would then overflow two workgroups per CU:
+    // there each tile is reconstructed right before its own products, and the
+    // other workgroup on the CU fills the matrix cores meanwhile.
+    constexpr bool PIPE = !(PROB && D == 64);
     using LT = LdsTile<D>;
     constexpr int BUF = LT::kFloats;
     // K (sweep 1) / V (sweep 2) tiles, double-buffered.  The two buffers are
@@ -148,6 +153,31 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
         if (qt & 1) { store_tile(accB, qt, true); track_tile(accB, qt, true); }
         else { store_tile(accA, qt, true); track_tile(accA, qt, true); }
     }
+    // Sweep 2's first V tile and this wave's first score tiles need no row
+    // statistic: their loads go out here, ahead of the extremes' re-reads
+    // below, so both wait on one memory latency.
+    float sv[16];
+    f32x4 sx[4];
+    LT::load(lds0, V, 0, T, tid);
+    if (active) {
+        if (PIPE) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const f32x4 x = *(const f32x4*)(tiles + p * 256 + lane * 4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sv[4 * p + j] = x[j];
+            }
+            if (qt > 0) {
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+                    sx[p] = __builtin_nontemporal_load((const f32x4*)(tiles + kTileElems + p * 256 + lane * 4));
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                sx[p] = __builtin_nontemporal_load((const f32x4*)(tiles + p * 256 + lane * 4));
+        }
+    }
     // Row extremes: the two lane halves of a query saw disjoint keys.  Each
     // half whose extreme equals the row's reads back its 16 stored scores of
     // the tile where that extreme first appeared and takes the first key
@@ -214,7 +244,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
 #pragma unroll
     for (int b = 0; b < (PROB ? NB : 1); ++b) olacc[b] = f32x16{};
 
-    float sv[16], wA[16], wlA[PROB ? 16 : 1], wB[16], wlB[PROB ? 16 : 1];
+    float wA[16], wlA[PROB ? 16 : 1], wB[16], wlB[PROB ? 16 : 1];
     auto recon = [&](int kt_t, auto diag_t, int r, float* w, float* wl) {
         // no contraction: every instantiation (with or without the Prob-STE
         // extras) rounds the weights and their sums identically
@@ -255,21 +285,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
     };
 
     // Score tiles go straight into registers, loaded one tile ahead of their
-    // reconstruction (sx), which itself runs one tile ahead of the products.
-    f32x4 sx[4];
-    LT::load(lds0, V, 0, T, tid);
-    if (active) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const f32x4 x = *(const f32x4*)(tiles + p * 256 + lane * 4);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sv[4 * p + j] = x[j];
-        }
-        if (qt > 0) {
-#pragma unroll
-            for (int p = 0; p < 4; ++p)
-                sx[p] = __builtin_nontemporal_load((const f32x4*)(tiles + kTileElems + p * 256 + lane * 4));
-        }
+    // reconstruction (sx), which itself runs one tile ahead of the products
+    // when PIPE.
+    if (PIPE && active) {
         if (qt == 0) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) recon(0, std::true_type{}, r, wA, wlA);
@@ -281,6 +299,11 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
     }
     wait_vmcnt<0>();
     __syncthreads();
+    // V^T operand: lane = head-dim column, one float per key (column reads)
+    auto v_operand = [&](const float* cur, float* xv) __attribute__((always_inline)) {
+#pragma unroll
+        for (int s2 = 0; s2 < 16 * NB; ++s2) xv[s2] = cur[LT::off(acc_row(s2 & 15, hl), 32 * (s2 >> 4) + li)];
+    };
     // tile kt: weights in (w, wl); reconstruct tile kt+1 into (wn, wln)
     auto sweep2 = [&](int kt, const float* cur, float* nxt, const float* w, const float* wl, float* wn, float* wln)
         __attribute__((always_inline)) {
@@ -305,10 +328,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
         // the score loads are issued here, ahead of this tile's work
         __builtin_amdgcn_sched_barrier(0);
         if (active && kt <= qt) {
-            // V^T operand: lane = head-dim column, one float per key (column reads)
             float xv[16 * NB];
-#pragma unroll
-            for (int s2 = 0; s2 < 16 * NB; ++s2) xv[s2] = cur[LT::off(acc_row(s2 & 15, hl), 32 * (s2 >> 4) + li)];
+            v_operand(cur, xv);
             auto mstep = [&](int s) {
                 const int b = s >> 4, kk = s & 15;
                 oacc[b] = mfma32x32x2(xv[s], w[kk], oacc[b]);
@@ -331,9 +352,57 @@ __global__ __launch_bounds__(kThreads, (D == 64 && !PROB ? 2 : 1)) void kia_forw
         else wait_vmcnt<0>();
         lds_barrier();
     };
+    // tile kt reconstructed into (wA, wlA), then its products
+    auto sweep2_serial = [&](int kt, const float* cur, float* nxt) __attribute__((always_inline)) {
+        const bool here = active && kt <= qt;
+        const bool prefetch = active && kt + 1 <= qt;
+        if (here) {
+            // scores of tile kt, loaded during the previous tile: the only
+            // vector memory operations of this wave still outstanding here
+            wait_vmcnt<0>();
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sv[4 * p + j] = sx[p][j];
+        }
+        if (kt < kt_end) LT::load(nxt, V, (kt + 1) * kTile, T, tid);
+        if (prefetch) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                sx[p] = __builtin_nontemporal_load(
+                    (const f32x4*)(tiles + (size_t)(kt + 1) * kTileElems + p * 256 + lane * 4));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (here) {
+            if (kt == qt) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) recon(kt, std::true_type{}, r, wA, wlA);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) recon(kt, std::false_type{}, r, wA, wlA);
+            }
+            float xv[16 * NB];
+            v_operand(cur, xv);
+#pragma unroll
+            for (int s = 0; s < 16 * NB; ++s) {
+                const int b = s >> 4, kk = s & 15;
+                oacc[b] = mfma32x32x2(xv[s], wA[kk], oacc[b]);
+                if (PROB) olacc[b] = mfma32x32x2(xv[s], wlA[kk], olacc[b]);
+            }
+        }
+        flush_sums();
+        if (prefetch) wait_vmcnt<4>();
+        else wait_vmcnt<0>();
+        lds_barrier();
+    };
     for (int kt = 0; kt <= kt_end; kt += 2) {
-        sweep2(kt, lds0, lds1, wA, wlA, wB, wlB);
-        if (kt + 1 <= kt_end) sweep2(kt + 1, lds1, lds0, wB, wlB, wA, wlA);
+        if constexpr (PIPE) {
+            sweep2(kt, lds0, lds1, wA, wlA, wB, wlB);
+            if (kt + 1 <= kt_end) sweep2(kt + 1, lds1, lds0, wB, wlB, wA, wlA);
+        } else {
+            sweep2_serial(kt, lds0, lds1);
+            if (kt + 1 <= kt_end) sweep2_serial(kt + 1, lds1, lds0);
+        }
     }
     W64 += __shfl_xor(W64, 32);
     const float W = (float)W64;
