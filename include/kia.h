@@ -145,7 +145,12 @@ kia_status kia_forward(const kia_params* p, int B, int H, int T, int d,
  * placement (section 3; App. B).  o and stats must come from kia_forward with
  * the same q, k, v, p and shape.  ws: scratch of kia_workspace_bytes(...)
  * bytes; on return it holds the tiles and row terms kia_workspace_layout
- * describes.  dq, dk, dv: outputs [B,H,T,d]. */
+ * describes.  dq, dk, dv: outputs [B,H,T,d].
+ * Where the row's grid has at most 32 intervals (MinMax or FWM under LERP or
+ * Nearest), the backward reads each score's grid value from a per-row table
+ * of the K+1 values instead of evaluating an exponential per score; the
+ * environment variable KIA_GRID_TABLE=0 (read at each call) selects the
+ * per-score exponential, with bitwise the same results. */
 kia_status kia_backward(const kia_params* p, int B, int H, int T, int d,
                         const float* q, const float* k, const float* v,
                         const float* o, const float* d_o,

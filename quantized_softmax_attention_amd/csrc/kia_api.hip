@@ -3,6 +3,7 @@
 // never synchronises and keeps no mutable global state.
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -111,6 +112,14 @@ kia_status record(const kia_ext* ext, int i, hipStream_t st) {
 bool exact(const kia_params* p) { return p->reconstruction >= KIA_REC_EXACT; }
 float tau_of(const kia_params* p) { return exact(p) ? 1.f : p->tau; }
 
+// KIA_GRID_TABLE=0 in the environment turns the row kernel's grid table off
+// (one exponential per score instead): the results are bitwise the same, so
+// the two can be compared by time and counters alone.
+bool grid_table_enabled() {
+    const char* e = getenv("KIA_GRID_TABLE");
+    return !(e && e[0] == '0' && e[1] == '\0');
+}
+
 kia::FwdConfig config_of(const kia_params* p, int d, bool dump) {
     kia::FwdConfig c;
     c.d = d;
@@ -118,7 +127,7 @@ kia::FwdConfig config_of(const kia_params* p, int d, bool dump) {
     c.rec = p->reconstruction;
     c.prob = prob_extras(p);
     c.dump = dump;
-    c.tab = kia::tab_capable(c.cal, c.rec) && p->n_intervals <= kia::kTabMaxK;
+    c.tab = kia::tab_capable(c.cal, c.rec) && p->n_intervals <= kia::kTabMaxK && grid_table_enabled();
     return c;
 }
 

@@ -233,8 +233,10 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
                             // the hard weight's grid point (past K only outside the FWM window)
                             pw = gt[tab_off((int)((CAL == CAL_FWM) ? fminf(rn, rg.Kf) : rn), li)] * iwc;
                         } else {
+                            // the table's values and products exactly, so both
+                            // paths store the same P
                             gc = fast_exp2(fmaf(-fi, rg.hl2, lc));
-                            pw = fast_exp2(fmaf(-rn, rg.hl2, lw));
+                            pw = fast_exp2(fmaf(-rn, rg.hl2, lc)) * iwc;
                         }
                         Gc = fmaf(dp[r], invWe, nd) * gc;
                     }

@@ -2,7 +2,8 @@
 // stored and of how far the operator's probabilities sit from the softmax of
 // the same scores ("Pretraining Transformers with Quantized Softmax in
 // Attention", section 4 "Geometry probe"; section 5.4; App. D.6).  It is a
-// row reduction over the score tiles with no matrix products: HBM-bound.
+// row reduction over the score tiles with no matrix products, bound by
+// memory traffic and by its per-score instruction issue.
 //
 // Fields, each an fp32 array over the B*H*T rows: span (max - min), native
 // width h (the operator's interval width: MinMax span/K, 0 on degenerate
@@ -21,13 +22,25 @@ namespace {
 
 constexpr int kGeoFields = 8;
 
-// One workgroup of four wavefronts per 32-row query tile; wave w takes the
-// key tiles kt = w, w+4, ...  Lane l owns query l%32; of every 32-key tile it
-// holds the 16 keys 8p + 4*(l/32) + j (p, j < 4), which the query-major
-// storage lays out as four float4 loads of one contiguous kilobyte per wave.
-// The two lanes of a row combine with one exchange, the four waves through
-// LDS.  Blocks run the longest rows first, across all heads.
-constexpr int kGeoWaves = 4;
+// One workgroup of eight wavefronts per 32-row query tile; wave w takes the
+// key tiles kt = w, w+8, ..., two at a time.  Lane l owns query l%32; of every
+// 32-key tile it holds the 16 keys 8p + 4*(l/32) + j (p, j < 4), which the
+// query-major storage lays out as four float4 loads of one contiguous kilobyte
+// per wave.  The two lanes of a row combine with one exchange, the waves
+// through LDS.  Blocks run the longest rows first, across all heads.
+//
+// Pass B needs the softmax normaliser Z of the whole row, so the tiles are
+// read twice, and the second read is arranged to hit L2 where it can: eight
+// waves per row block halve a block's lifetime (and so the tiles it holds in
+// L2), pass B walks each wave's tiles in the reverse order of pass A, starting
+// with the ones pass A read last, and its loads, each tile's last use, carry
+// the non-temporal policy so they do not evict tiles other blocks still
+// re-read.
+constexpr int kGeoWaves = 8;
+
+// u < this value exactly when floor(u + 1/2) == 0 in fp32, for u >= 0: the
+// largest float below 1/2 plus 1/2 rounds (to even) up to 1
+constexpr float kTopU = 0x1.fffffep-2f;
 
 template <int CAL, int REC>
 __global__ __launch_bounds__(kGeoWaves * kWave) void kia_geometry_kernel(GeoArgs a) {
@@ -46,6 +59,24 @@ __global__ __launch_bounds__(kGeoWaves * kWave) void kia_geometry_kernel(GeoArgs
     const size_t row = (size_t)bh * a.T + (qvalid ? qrow : 0);
     const int64_t tiles_per_head = (int64_t)a.n_t * (a.n_t + 1) / 2;
     const float* tiles = a.tiles + ((size_t)bh * tiles_per_head + tile_index(qt, 0)) * kTileElems;
+    auto load_tile = [&](int kt, f32x4* x) {
+        const float* tp = tiles + (size_t)kt * kTileElems;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) x[p] = *(const f32x4*)(tp + p * 256 + lane * 4);
+    };
+    // pass B's reads are each tile's last use
+    auto load_tile_last = [&](int kt, f32x4* x) {
+        const float* tp = tiles + (size_t)kt * kTileElems;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) x[p] = __builtin_nontemporal_load((const f32x4*)(tp + p * 256 + lane * 4));
+    };
+    // reduction of per-wave row partials in a fixed order
+    auto wave_sum = [&](int f) {
+        double r = 0.0;
+#pragma unroll
+        for (int w = 0; w < kGeoWaves; ++w) r += s_sum[f][w][qi];
+        return r;
+    };
 
     // pass A: row min and the softmax normaliser Z (the max comes from the
     // forward's row statistics)
@@ -76,14 +107,8 @@ __global__ __launch_bounds__(kGeoWaves * kWave) void kia_geometry_kernel(GeoArgs
     for (int kt = wv; kt <= qt; kt += 2 * kGeoWaves) {
         const int kt2 = kt + kGeoWaves;
         f32x4 x[4], y[4];
-        const float* tp = tiles + (size_t)kt * kTileElems;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) x[p] = *(const f32x4*)(tp + p * 256 + lane * 4);
-        if (kt2 <= qt) {
-            const float* tq = tiles + (size_t)kt2 * kTileElems;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) y[p] = *(const f32x4*)(tq + p * 256 + lane * 4);
-        }
+        load_tile(kt, x);
+        if (kt2 <= qt) load_tile(kt2, y);
         run_a(kt, x);
         if (kt2 <= qt) run_a(kt2, y);
     }
@@ -94,8 +119,9 @@ __global__ __launch_bounds__(kGeoWaves * kWave) void kia_geometry_kernel(GeoArgs
         s_sum[0][wv][qi] = Z;
     }
     __syncthreads();
-    mn = fminf(fminf(s_mn[0][qi], s_mn[1][qi]), fminf(s_mn[2][qi], s_mn[3][qi]));
-    Z = (s_sum[0][0][qi] + s_sum[0][1][qi]) + (s_sum[0][2][qi] + s_sum[0][3][qi]);
+#pragma unroll
+    for (int w = 0; w < kGeoWaves; ++w) mn = fminf(mn, s_mn[w][qi]);
+    Z = wave_sum(0);
     __syncthreads();
 
     // the operator's grid; the exact reference lays a MinMax grid for the
@@ -104,15 +130,17 @@ __global__ __launch_bounds__(kGeoWaves * kWave) void kia_geometry_kernel(GeoArgs
     const RowGrid rg = make_row_grid(m, mn, a.K, a.tau, GCAL == CAL_MINMAX ? CAL_MINMAX : CAL_FWM);
     const float W = qvalid ? a.row_w[row] : 1.f;
     const float invW = 1.f / W;
-    const float logW = (float)log((double)W);
     const float invZ = (float)(1.0 / Z);
-    const float logZ = (float)log(Z);
 
-    // pass B: entropies, total variation, top-bucket mass
-    double tv = 0.0, hp = 0.0, hq = 0.0, top = 0.0;
+    // pass B: total variation needs Z per key; the entropies and the top mass
+    // are accumulated as sums divided by W or Z at the end:
+    //   H(P) = ln W - (1/W) sum w ln w,  H(q) = ln Z - (1/Z) sum e (s - m),
+    //   top = (1/Z) sum over the top bucket of e
+    // (sum w = W up to rounding: the forward's W sums these same weights)
+    double tv = 0.0, wlw = 0.0, es = 0.0, etop = 0.0;
     auto pass_b = [&](int kt, const f32x4* x, auto diag_t) {
         constexpr bool DIAG = decltype(diag_t)::value;
-        float tvt = 0.f, hpt = 0.f, hqt = 0.f, topt = 0.f;
+        float tvt = 0.f, wlwt = 0.f, est = 0.f, etopt = 0.f;
 #pragma unroll
         for (int p = 0; p < 4; ++p)
 #pragma unroll
@@ -120,77 +148,71 @@ __global__ __launch_bounds__(kGeoWaves * kWave) void kia_geometry_kernel(GeoArgs
                 const int key = kt * kTile + 8 * p + 4 * hl + j;
                 if (DIAG && key > qrow) continue;
                 const float s = x[p][j];
-                const float xe = (s - m) * kLog2e;
+                const float sm = s - m;
+                const float xe = sm * kLog2e;
                 const float e = fast_exp2(xe);
                 const float u = (rg.m - s) * rg.invh;
-                // w and its natural log; where w = exp2(x), ln w = x ln 2
-                float w, lw;
+                // w and w ln w; where w = exp2(x), ln w = x ln 2
+                float w, wl;
                 if (REC == REC_EXACT) {
                     w = e;
-                    lw = xe * kLn2;
+                    wl = e * (xe * kLn2);
                 } else if (softmax_rec(REC)) {
                     w = round_exp<REC>(e);
-                    lw = __logf(w);
+                    wl = w > 0.f ? w * __logf(w) : 0.f;
                 } else if (REC == REC_NEAREST) {
                     const float xr = -floorf(u + 0.5f) * rg.hl2;
                     const bool keep = (CAL == CAL_FWM) ? (u <= rg.Kf) : true;
                     w = keep ? fast_exp2(xr) : 0.f;
-                    lw = xr * kLn2;
+                    wl = w > 0.f ? w * (xr * kLn2) : 0.f;
                 } else {
                     const bool keep = (CAL == CAL_FWM) ? (u <= rg.Kf) : true;
                     const float fi = floorf(u);
                     const float g = fast_exp2(-fi * rg.hl2);
                     w = keep ? g * fmaf(fi - u, rg.c, 1.f) : 0.f;
-                    lw = __logf(w);
+                    wl = w > 0.f ? w * __logf(w) : 0.f;
                 }
-                const float pw = w * invW;
-                const float qs = e * invZ;
-                tvt += fabsf(pw - qs);
-                if (w > 0.f) hpt -= pw * (lw - logW);
-                hqt -= qs * ((s - m) - logZ);
-                if (floorf(u + 0.5f) == 0.f) topt += qs;
+                tvt += fabsf(w * invW - e * invZ);
+                wlwt += wl;
+                est = fmaf(e, sm, est);
+                etopt += (u < kTopU) ? e : 0.f;
             }
         tv += (double)tvt;
-        hp += (double)hpt;
-        hq += (double)hqt;
-        top += (double)topt;
+        wlw += (double)wlwt;
+        es += (double)est;
+        etop += (double)etopt;
     };
     auto run_b = [&](int kt, const f32x4* x) {
         if (kt < qt) pass_b(kt, x, std::false_type{});
         else pass_b(kt, x, std::true_type{});
     };
-    for (int kt = wv; kt <= qt; kt += 2 * kGeoWaves) {
-        const int kt2 = kt + kGeoWaves;
-        f32x4 x[4], y[4];
-        const float* tp = tiles + (size_t)kt * kTileElems;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) x[p] = *(const f32x4*)(tp + p * 256 + lane * 4);
-        if (kt2 <= qt) {
-            const float* tq = tiles + (size_t)kt2 * kTileElems;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) y[p] = *(const f32x4*)(tq + p * 256 + lane * 4);
+    if (wv <= qt) {
+        // the pairs of pass A, last pair first, the later tile of a pair first
+        for (int kt = wv + ((qt - wv) / (2 * kGeoWaves)) * (2 * kGeoWaves); kt >= wv; kt -= 2 * kGeoWaves) {
+            const int kt2 = kt + kGeoWaves;
+            f32x4 x[4], y[4];
+            if (kt2 <= qt) load_tile_last(kt2, y);
+            load_tile_last(kt, x);
+            if (kt2 <= qt) run_b(kt2, y);
+            run_b(kt, x);
         }
-        run_b(kt, x);
-        if (kt2 <= qt) run_b(kt2, y);
     }
     tv += __shfl_xor(tv, 32);
-    hp += __shfl_xor(hp, 32);
-    hq += __shfl_xor(hq, 32);
-    top += __shfl_xor(top, 32);
+    wlw += __shfl_xor(wlw, 32);
+    es += __shfl_xor(es, 32);
+    etop += __shfl_xor(etop, 32);
     if (hl == 0) {
         s_sum[0][wv][qi] = tv;
-        s_sum[1][wv][qi] = hp;
-        s_sum[2][wv][qi] = hq;
-        s_sum[3][wv][qi] = top;
+        s_sum[1][wv][qi] = wlw;
+        s_sum[2][wv][qi] = es;
+        s_sum[3][wv][qi] = etop;
     }
     __syncthreads();
     if (!qvalid) return;
     const size_t n_rows = (size_t)a.BH * a.T;
     float* g = a.geo + row;
     if (wv == 0 && hl == 0) {
-        double r[4];
-#pragma unroll
-        for (int f = 0; f < 4; ++f) r[f] = (s_sum[f][0][qi] + s_sum[f][1][qi]) + (s_sum[f][2][qi] + s_sum[f][3][qi]);
+        const double r_tv = wave_sum(0), r_wlw = wave_sum(1), r_es = wave_sum(2), r_top = wave_sum(3);
         const float span = m - mn;
         float h;
         if (GCAL == CAL_MINMAX) {
@@ -200,10 +222,10 @@ __global__ __launch_bounds__(kGeoWaves * kWave) void kia_geometry_kernel(GeoArgs
         }
         g[0] = span;
         g[1 * n_rows] = h;
-        g[4 * n_rows] = (float)r[1];
-        g[5 * n_rows] = (float)r[2];
-        g[6 * n_rows] = (float)(0.5 * r[0]);
-        g[7 * n_rows] = (float)r[3];
+        g[4 * n_rows] = (float)(log((double)W) - r_wlw / (double)W);
+        g[5 * n_rows] = (float)(log(Z) - r_es / Z);
+        g[6 * n_rows] = (float)(0.5 * r_tv);
+        g[7 * n_rows] = (float)(r_top / Z);
     } else if (wv == 1) {
         // norms of the unscaled projections at this position: Q on the lower
         // half-wave, K on the upper

@@ -131,3 +131,38 @@ def test_autograd_op_matches_direct_calls(kw):
     assert torch.equal(o.detach(), o_ref)
     for name, got, ref in (("dq", dq, dq_ref), ("dk", dk, dk_ref), ("dv", dv, dv_ref)):
         assert torch.equal(got, ref), name
+
+
+TABLE_VARIANTS = [dict(K=32), dict(K=32, reconstruction="nearest"),
+                  dict(K=4, calibration="fwm", reconstruction="nearest", surrogate="prob"),
+                  dict(K=16, calibration="fwm", grad_rule="detach"), dict(K=16, d128=True),
+                  dict(K=4, calibration="fwm", reconstruction="nearest", surrogate="prob", grad_rule="p1", d128=True)]
+
+
+@pytest.mark.parametrize("kw", TABLE_VARIANTS, ids=lambda kw: "-".join(f"{k}={v}" for k, v in kw.items()))
+def test_grid_table_matches_per_score_exponential(kw, monkeypatch):
+    """The row kernel's per-row grid table holds exactly the values the
+    per-score exponential computes (same expression, same inputs), so the
+    backward with KIA_GRID_TABLE=0 is bitwise the same."""
+    import torch
+    import quantized_softmax_attention_amd as kia
+    p, w = _variant(kw)
+    x = _tensors(w=w)
+    with_table, without = _alloc(kia, x, p), _alloc(kia, x, p)
+    print(f"[case] grid table on / off {p}", flush=True)
+    monkeypatch.delenv("KIA_GRID_TABLE", raising=False)
+    _step(kia, x, p, with_table)
+    monkeypatch.setenv("KIA_GRID_TABLE", "0")
+    _step(kia, x, p, without)
+    monkeypatch.delenv("KIA_GRID_TABLE")
+    torch.cuda.synchronize()
+    for name, ga, gb in zip(("o", "dq", "dk", "dv"), (with_table[0], with_table[2], with_table[3], with_table[4]),
+                            (without[0], without[2], without[3], without[4])):
+        assert torch.equal(ga, gb), name
+    # the stored P and dS tiles too
+    B, H, T, _ = x[0].shape
+    WL = kia.kia_workspace_layout_query(p, *x[0].shape)
+    for off in (WL.probs, WL.dscores):
+        ta = kia.kia_tiles_to_dense(B, H, T, with_table[5][off:], True)
+        tb = kia.kia_tiles_to_dense(B, H, T, without[5][off:], True)
+        assert torch.equal(ta, tb)
