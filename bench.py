@@ -9,10 +9,14 @@ ONE JSON line.  Throughput counts algorithmic work only: 12*d flop per causal
 (query, key) pair -- forward QK^T and PV, backward dP, dV, dQ, dK -- and not
 the masked upper triangle or any recomputation.
 
-Per-kernel times come from HIP events recorded by the library on the launch
-stream around each kernel inside the timed loop; the dominant kernel's
-algorithmic flops per launch over its mean duration is the roofline figure
-(fp32 matrix peak of the MI355X: 157.3 TFLOP/s).  Its HBM traffic is taken
+The K timed steps replay the step captured once as a HIP graph (the
+library's kernels back to back from one host call per step), so the
+throughput measures the GPU rather than the Python binding's per-call checks;
+the line also reports the same K steps launched eagerly (through kia.Step,
+which checks the buffers once) and the host time spent enqueuing them.  Per-kernel times come from HIP events recorded by the
+library on the launch stream around each kernel of those eager steps; the
+dominant kernel's algorithmic flops per launch over its mean duration is the
+roofline figure (fp32 matrix peak of the MI355X: 157.3 TFLOP/s).  Its HBM traffic is taken
 from the committed rocprofv3 counter summary when that summary was made from
 the current kernel sources, else reported as null.
 
@@ -411,26 +415,57 @@ def main():
         kia.kia_forward(tq, tk, tv, params, o=o, stats=stats, events=evf)
         kia.kia_backward(tq, tk, tv, o, tdo, stats, params, dq=dq, dk=dk, dv=dv, ws=ws, events=evb)
 
+    # The step as a HIP graph: its three (or, under P1, five) kernels replay
+    # back to back from one host call, so the timed steps measure the GPU and
+    # not the Python binding's per-call checks (which on a slow host can take
+    # longer than the GPU's step).  Captured on a side stream after one eager
+    # step there; the library launches only on the stream it is given and
+    # allocates nothing with every buffer passed in.
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        step()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            step()
+    torch.cuda.synchronize()
+
     # spin-up: the same step, untimed, until the clocks have settled
     spin_steps = 0
     t_spin = time.perf_counter()
     while (time.perf_counter() - t_spin) * 1e3 < args.spinup_ms:
         for _ in range(20):
-            step()
+            graph.replay()
         spin_steps += 20
         torch.cuda.synchronize()
     spin_ms = (time.perf_counter() - t_spin) * 1e3
     for _ in range(args.warmup):
-        step()
-    ev = HipEvents()
-    evs = [(ev.make(2), ev.make(4)) for _ in range(args.steps)]
+        graph.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for evf, evb in evs:
-        step(evf, evb)
+    for _ in range(args.steps):
+        graph.replay()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
     ms_step = wall_ms / args.steps
+
+    # Per-kernel times: the same number of eager steps with HIP events the
+    # library records on its stream around each kernel.  The host time to
+    # enqueue them is reported too: when it exceeds the GPU's step, eager
+    # launching would leave the GPU idle between steps.
+    # (kia.Step checks the buffers once and then only passes the stored
+    # arguments to the C ABI, so the host keeps ahead of the GPU)
+    fast = kia.Step(tq, tk, tv, tdo, params, o, stats, dq, dk, dv, ws)
+    ev = HipEvents()
+    evs = [(ev.make(2), ev.make(4)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for evf, evb in evs:
+        fast(evf, evb)
+    host_ms = (time.perf_counter() - t1) * 1e3 / args.steps
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t1) * 1e3 / args.steps
 
     per_kernel = {name: [] for name in KERNELS}
     per_step = []
@@ -517,6 +552,8 @@ def main():
         "kernel_ms": {n: round(t, 4) for n, t in kern_ms.items()},
         "kernel_ms_median": {n: round(t, 4) for n, t in kern_median.items()},
         "ms_per_step_median": round(step_median, 4),
+        "launch": "hip_graph",
+        "eager": {"ms_per_step": round(eager_ms, 4), "host_enqueue_ms_per_step": round(host_ms, 4)},
         "spinup": {"ms": round(spin_ms, 1), "steps": spin_steps},
     }
     if peak is not None:

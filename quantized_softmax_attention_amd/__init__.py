@@ -207,6 +207,46 @@ def kia_backward(q, k, v, o, do, stats, params: Params, dq=None, dk=None, dv=Non
     return dq, dk, dv, ws
 
 
+class Step:
+    """One forward + backward over fixed buffers, for loops that launch the
+    same step many times.  The buffers are checked once, here, by one
+    kia_forward and one kia_backward call (which also run the step); each
+    later call passes the stored arguments straight to the C ABI
+    (kia_forward_ext / kia_backward_ext when HIP events are given), on the
+    stream that was current here (or `stream`).  Call it with the tensors'
+    device current; the tensors are kept alive by the object."""
+
+    def __init__(self, q, k, v, do, params: Params, o, stats, dq, dk, dv, ws, stream=None):
+        kia_forward(q, k, v, params, o=o, stats=stats, stream=stream)
+        kia_backward(q, k, v, o, do, stats, params, dq=dq, dk=dk, dv=dv, ws=ws, stream=stream)
+        B, H, T, d = _shape(q)
+        self._lib = _lib.load()
+        self._cp = params.c()
+        st = _stream(stream, q.device)
+        cp = ctypes.byref(self._cp)
+        self._fargs = (cp, B, H, T, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                       stats.data_ptr(), _nbytes(stats), st)
+        self._bargs = (cp, B, H, T, d, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                       stats.data_ptr(), _nbytes(stats), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                       ws.data_ptr(), _nbytes(ws), st)
+        self._keep = (q, k, v, do, o, stats, dq, dk, dv, ws)
+
+    def __call__(self, events_f=None, events_b=None):
+        lib = self._lib
+        if events_f is None:
+            st = lib.kia_forward(*self._fargs)
+        else:
+            st = lib.kia_forward_ext(*self._fargs, ctypes.byref(_ext(events_f, None)))
+        if st:
+            raise KiaError(st, "kia_forward")
+        if events_b is None:
+            st = lib.kia_backward(*self._bargs)
+        else:
+            st = lib.kia_backward_ext(*self._bargs, ctypes.byref(_ext(events_b, None)))
+        if st:
+            raise KiaError(st, "kia_backward")
+
+
 def kia_backward_noalloc(q, k, v, o, do, stats, params: Params, dq=None, dk=None, dv=None, stream=None):
     """kia_backward without a workspace: the library takes it from its own
     per-device scratch (include/kia.h, kia_backward_noalloc) and allocates
@@ -334,4 +374,4 @@ def kia_abi_version() -> int:
 
 __all__ = ["Params", "KiaError", "kia_forward", "kia_backward", "kia_stats_bytes",
            "kia_workspace_bytes", "kia_stats_layout_query", "kia_workspace_layout_query",
-           "kia_geometry", "GEOMETRY_FIELDS", "kia_tiles_to_dense", "kia_abi_version", "kia_attention"]
+           "kia_geometry", "GEOMETRY_FIELDS", "kia_tiles_to_dense", "kia_abi_version", "kia_attention", "Step"]

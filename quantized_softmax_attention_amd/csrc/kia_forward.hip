@@ -22,15 +22,22 @@
 
 namespace kia {
 
-template <int D, int CAL, int REC, bool PROB, bool DUMP>
-__global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_forward_kernel(FwdArgs a) {
+// Sweep 2 order.  SER: each tile is reconstructed right before its own
+// products, with one set of weights, and the other workgroup on the CU fills
+// the matrix cores meanwhile.  Otherwise (d = 64 without the Prob-STE extras,
+// rows of at most kPipeMaxTiles tiles) tile kt+1 is reconstructed while the
+// products of tile kt run, interleaved instruction by instruction.  The
+// serial order needs fewer registers (two workgroups per CU also at d = 128,
+// and with the Prob-STE extras at d = 64) and was measured faster on long
+// rows; the interleaved one on the GPT-2-shaped rows of 1024 keys.
+constexpr int kPipeMaxTiles = 32;
+
+template <int D, int CAL, int REC, bool PROB, bool DUMP, bool SER>
+__global__ __launch_bounds__(kThreads, (D == 128 && PROB) ? 1 : 2) void kia_forward_kernel(FwdArgs a) {
     static_assert(D % 32 == 0, "head dim must be a multiple of 32");
+    static_assert(SER || (D == 64 && !PROB), "the interleaved order exists for d = 64 without Prob-STE only");
     constexpr int NB = D / 32;  // 32-wide blocks of the head dim
-    // Sweep 2 reconstructs one tile ahead of the products (PIPE) unless the
-    // Prob-STE extras at d = 64 would then overflow two workgroups per CU:
-    // there each tile is reconstructed right before its own products, and the
-    // other workgroup on the CU fills the matrix cores meanwhile.
-    constexpr bool PIPE = !(PROB && D == 64);
+    constexpr bool PIPE = !SER;
     using LT = LdsTile<D>;
     constexpr int BUF = LT::kFloats;
     // K (sweep 1) / V (sweep 2) tiles, double-buffered.  The two buffers are
@@ -448,8 +455,14 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_forward_kerne
 template <int D, int CAL, int REC, bool PROB, bool DUMP>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
     const int n_blk = (a.n_t + kBlockTiles - 1) / kBlockTiles;
-    hipLaunchKernelGGL((kia_forward_kernel<D, CAL, REC, PROB, DUMP>), dim3((unsigned)(a.BH * n_blk)),
-                       dim3(kThreads), 0, s, a);
+    const dim3 grid((unsigned)(a.BH * n_blk));
+    if constexpr (D == 64 && !PROB) {
+        if (a.n_t <= kPipeMaxTiles) {
+            hipLaunchKernelGGL((kia_forward_kernel<D, CAL, REC, PROB, DUMP, false>), grid, dim3(kThreads), 0, s, a);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((kia_forward_kernel<D, CAL, REC, PROB, DUMP, true>), grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -94,6 +94,17 @@ def test_small_d128_rules(cal, rec, ste, rule):
     check(SMALL128, P(K=16, tau=6.0, calibration=cal, reconstruction=rec, surrogate=ste, grad_rule=rule))
 
 
+# Rows past 32 key tiles take the forward's serial sweep order at d = 64
+# (rows of up to 1024 keys the interleaved one): one ragged head of each
+# operator just past that length, every decision checked.
+LONG_ROWS = Workload("long_rows_ragged", 1, 1, 1057, 64, "scaled", q_scale=2.0)
+
+
+@pytest.mark.parametrize("cal,rec,ste", COMBOS)
+def test_rows_past_the_interleaved_length(cal, rec, ste):
+    check(LONG_ROWS, P(K=8, tau=6.0, calibration=cal, reconstruction=rec, surrogate=ste))
+
+
 @pytest.mark.parametrize("T", [1, 2, 31, 32, 33, 64, 97])
 def test_edge_lengths(T):
     w = Workload(f"len{T}", 1, 3, T, 64, "scaled", q_scale=2.0)

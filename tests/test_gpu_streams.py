@@ -166,3 +166,25 @@ def test_grid_table_matches_per_score_exponential(kw, monkeypatch):
         ta = kia.kia_tiles_to_dense(B, H, T, with_table[5][off:], True)
         tb = kia.kia_tiles_to_dense(B, H, T, without[5][off:], True)
         assert torch.equal(ta, tb)
+
+
+@pytest.mark.parametrize("kw", VARIANTS, ids=lambda kw: "-".join(f"{k}={v}" for k, v in kw.items()))
+def test_prepared_step_matches_direct_calls(kw):
+    """kia.Step (buffers checked once, then the C ABI called with stored
+    arguments) computes exactly what kia_forward + kia_backward compute."""
+    import torch
+    import quantized_softmax_attention_amd as kia
+    p, w = _variant(kw)
+    x = _tensors(w=w)
+    direct, prepared = _alloc(kia, x, p), _alloc(kia, x, p)
+    print(f"[case] prepared step {p}", flush=True)
+    _step(kia, x, p, direct)
+    q, k, v, do = x
+    o, st, dq, dk, dv, ws = prepared
+    step = kia.Step(q, k, v, do, p, o, st, dq, dk, dv, ws)
+    for t in (o, dq, dk, dv):
+        t.fill_(float("nan"))
+    step()
+    torch.cuda.synchronize()
+    for name, ga, gb in zip(("o", "dq", "dk", "dv"), (direct[0], direct[2], direct[3], direct[4]), (o, dq, dk, dv)):
+        assert torch.equal(ga, gb), name
