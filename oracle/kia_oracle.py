@@ -73,6 +73,17 @@ Readings where the pages leave a step open:
       softmax of the same scores; their total variation (1/2) sum |P - softmax|;
       and the softmax mass of the top rounding bucket, the keys whose Nearest
       point on that grid is 0 (u = (m - s)/h < 1/2; every key when h = 0).
+  R15 Scores are formed key by key as an fp64 sum over the head dimension in
+      index order (not a library matrix product, whose blocking may differ
+      between keys), so keys with equal vectors score exactly equal and the
+      tie rule R3 applies to them.
+  R16 Decisions (LERP segment, Nearest point, FWM window edge, the rounding
+      direction of a rounded exponential) may be supplied per key instead of
+      taken from u (the `decisions` argument): the pages define each decision
+      on the real-valued u, and where two finite-precision evaluations of u
+      fall on either side of a boundary both decisions read the pages
+      correctly.  Tests use this only with decisions they have shown to be
+      admissible for that key; with no override the oracle decides itself.
 
 Parity: every function below is pinned by the CPU tests (closed forms,
 brute force, finite differences, an autograd re-expression, the softmax
