@@ -156,6 +156,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
             LT::load(nxt, V, (kt + 1) * kTile, T, tid);
             LT::load(nxt + LT::kFloats, Kp, (kt + 1) * kTile, T, tid);
         }
+        // the staging loads stay ahead of every later memory operation of the
+        // step (the wait at its end counts the P / dS stores behind them)
+        __builtin_amdgcn_sched_barrier(0);
         // this tile's scores straight into registers, after the staging loads;
         // they are first needed after the dP products
         f32x4 sx[4];

@@ -132,6 +132,9 @@ __global__ __launch_bounds__(kThreads, (D == 128 && PROB) ? 1 : 2) void kia_forw
     auto sweep1 = [&](int kt, const float* cur, float* nxt, f32x16& acc, const f32x16& prv)
         __attribute__((always_inline)) {
         if (kt < kt_end) LT::load(nxt, Kp, (kt + 1) * kTile, T, tid);
+        // the staging loads stay ahead of every later memory operation of the
+        // step: the wait at its end counts only the score stores behind them
+        __builtin_amdgcn_sched_barrier(0);
         const bool stores = active && kt <= qt && kt > 0;
         if (active && kt <= qt) {
             f32x4 xk[D / 8];
@@ -326,6 +329,9 @@ __global__ __launch_bounds__(kThreads, (D == 128 && PROB) ? 1 : 2) void kia_forw
                 for (int j = 0; j < 4; ++j) sv[4 * p + j] = sx[p][j];
         }
         if (kt < kt_end) LT::load(nxt, V, (kt + 1) * kTile, T, tid);
+        // the staging loads stay ahead of the score loads: the wait at the end
+        // of the step leaves only those 4 in flight
+        __builtin_amdgcn_sched_barrier(0);
         if (prefetch) {
 #pragma unroll
             for (int p = 0; p < 4; ++p)
@@ -373,6 +379,9 @@ __global__ __launch_bounds__(kThreads, (D == 128 && PROB) ? 1 : 2) void kia_forw
                 for (int j = 0; j < 4; ++j) sv[4 * p + j] = sx[p][j];
         }
         if (kt < kt_end) LT::load(nxt, V, (kt + 1) * kTile, T, tid);
+        // the staging loads stay ahead of the score loads: the wait at the end
+        // of the step leaves only those 4 in flight
+        __builtin_amdgcn_sched_barrier(0);
         if (prefetch) {
 #pragma unroll
             for (int p = 0; p < 4; ++p)
