@@ -114,10 +114,13 @@ typedef struct kia_stats_layout {
  * the score gradient dS (calibration terms included) as tiles in key-major
  * order (per (b, h): tile (qt, kt) at the same index as the score tiles), and
  * the per-row calibration terms the gradient rule routed to the argmax key
- * (cm) and the argmin key (cn), fp32 [B*H*T].  Under KIA_GRAD_P1, cm holds
- * the subtracted row mean and cn is 0, and two more sections hold the causal
- * prefix sums of K ([B,H,T,d] fp32, prefix_k) and per-32-row chunk sums of K
- * (chunk_k); both offsets are 0 under the other rules. */
+ * (cm) and the argmin key (cn), fp32 [B*H*T].  Under KIA_GRAD_P1 the dS tiles
+ * hold the detached gradient, cm holds the row mean the rule subtracts from
+ * it (the projected gradient is dS - cm on each row's causal keys; dQ and dK
+ * include the subtraction) and cn is 0; two more sections serve as scratch
+ * for the P1 sums: [B,H,T,d] fp32 (prefix_k: the causal prefix sums of K,
+ * then the suffix sums of cm_t Q_t) and per-32-row chunk sums (chunk_k);
+ * both offsets are 0 under the other rules. */
 typedef struct kia_workspace_layout {
     size_t total_bytes;
     size_t probs;
@@ -182,7 +185,7 @@ kia_status kia_backward_noalloc(const kia_params* p, int B, int H, int T, int d,
  * hipEvent_t (as void*) recorded on `stream` around each kernel: forward
  * uses 2 (start/end of its one kernel), backward 4 (around its two kernels,
  * in launch order; under KIA_GRAD_P1 the first interval also covers the
- * key prefix-sum and row-centring launches).  idx_dump (forward only): NULL
+ * launches of the key prefix sums and of the query suffix sums).  idx_dump (forward only): NULL
  * or int32 [B,H,T,T]; for every causal pair the kernel writes the grid index
  * it used (the LERP segment, or the Nearest grid point), -1 for keys outside
  * the FWM window; 0 under KIA_REC_EXACT (no grid); under the rounded

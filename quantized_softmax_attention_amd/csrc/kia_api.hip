@@ -256,7 +256,6 @@ Shape slices_of(const Shape& s, int64_t n) {
 kia_status run_backward(const kia_params* p, const Shape& s, int64_t s0, int64_t n, const BwdPtrs& b, char* ws,
                         const kia_ext* ext, hipStream_t hs) {
     const bool p1 = p->grad_rule == KIA_GRAD_P1;
-    if (p1 && n * s.tiles_per_head > INT32_MAX) return KIA_ERR_SHAPE;  // one-dimensional grid of the centring kernel
     kia_stats_layout L;
     stats_layout(p, s, &L);
     const Shape c = slices_of(s, n);
@@ -284,6 +283,7 @@ kia_status run_backward(const kia_params* p, const Shape& s, int64_t s0, int64_t
     a.row_cn = (float*)(ws + WL.row_cn);
     a.prefix_k = p1 ? (float*)(ws + WL.prefix_k) : nullptr;
     a.chunk_k = p1 ? (float*)(ws + WL.chunk_k) : nullptr;
+    a.suffix_q = a.prefix_k;  // reused once the row kernel has read the prefix sums
     a.BH = (int)n; a.T = (int)s.T; a.n_t = (int)s.n_t; a.K = p->n_intervals;
     a.tau = tau_of(p);
     a.scale = 1.f / sqrtf((float)s.d);
@@ -294,7 +294,7 @@ kia_status run_backward(const kia_params* p, const Shape& s, int64_t s0, int64_t
     if ((st = record(ext, 0, hs)) != KIA_OK) return st;
     if (p1 && kia::launch_key_prefix((int)s.d, a, hs) != hipSuccess) return KIA_ERR_HIP;
     if (kia::launch_backward_rows(cfg, a, hs) != hipSuccess) return KIA_ERR_HIP;
-    if (p1 && kia::launch_center_rows(a, hs) != hipSuccess) return KIA_ERR_HIP;
+    if (p1 && kia::launch_query_suffix((int)s.d, a, hs) != hipSuccess) return KIA_ERR_HIP;
     if ((st = record(ext, 1, hs)) != KIA_OK) return st;
     if ((st = record(ext, 2, hs)) != KIA_OK) return st;
     if (kia::launch_backward_cols((int)s.d, a, hs) != hipSuccess) return KIA_ERR_HIP;

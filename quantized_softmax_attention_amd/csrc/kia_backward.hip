@@ -485,13 +485,19 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_cols
     if (active && krow < T) {
         float* dkrow = a.dk + head + (size_t)krow * D;
         float* dvrow = a.dv + head + (size_t)krow * D;
+        // P1: the row means enter dK as -sum_{t >= j} mu_t Q_t (the dS tiles
+        // hold the detached gradient)
+        const bool p1 = a.rule == GRAD_P1;
+        const float* sqrow = p1 ? a.suffix_q + head + (size_t)krow * D : nullptr;
 #pragma unroll
         for (int b = 0; b < NB; ++b)
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 const int c = 32 * b + 8 * p + 4 * hl;
-                *(f32x4*)(dkrow + c) = f32x4{dk[b][4 * p] * a.scale, dk[b][4 * p + 1] * a.scale,
-                                             dk[b][4 * p + 2] * a.scale, dk[b][4 * p + 3] * a.scale};
+                f32x4 sq = {0.f, 0.f, 0.f, 0.f};
+                if (p1) sq = *(const f32x4*)(sqrow + c);
+                *(f32x4*)(dkrow + c) = f32x4{(dk[b][4 * p] - sq[0]) * a.scale, (dk[b][4 * p + 1] - sq[1]) * a.scale,
+                                             (dk[b][4 * p + 2] - sq[2]) * a.scale, (dk[b][4 * p + 3] - sq[3]) * a.scale};
                 *(f32x4*)(dvrow + c) = f32x4{dv[b][4 * p], dv[b][4 * p + 1], dv[b][4 * p + 2], dv[b][4 * p + 3]};
             }
     }

@@ -45,8 +45,10 @@ struct BwdArgs {
     float* dscores;      // key-major dS tiles (calibration terms folded in)
     float* row_cm;       // P1: the subtracted row mean
     float* row_cn;
-    float* prefix_k;     // P1 only: sum_{j <= t} K_j per row, [BH, T, d]
-    float* chunk_k;      // P1 only: per-32-row chunk sums of K, [BH, n_t, d]
+    float* prefix_k;     // P1 only: sum_{j <= t} K_j per row, [BH, T, d] (read by the row kernel)
+    float* chunk_k;      // P1 only: per-32-row chunk sums of K, then of mu_t Q_t, [BH, n_t, d]
+    float* suffix_q;     // P1 only: sum_{t' >= t} mu_t' Q_t' per row, [BH, T, d] (the
+                         // prefix_k memory, rewritten after the row kernel; read by the column kernel)
     int BH, T, n_t, K;
     float tau, scale;
     int rule;
@@ -73,7 +75,7 @@ hipError_t launch_forward(const FwdConfig& c, const FwdArgs& a, hipStream_t s);
 hipError_t launch_backward_rows(const FwdConfig& c, const BwdArgs& a, hipStream_t s);
 hipError_t launch_backward_cols(int d, const BwdArgs& a, hipStream_t s);
 hipError_t launch_key_prefix(int d, const BwdArgs& a, hipStream_t s);
-hipError_t launch_center_rows(const BwdArgs& a, hipStream_t s);
+hipError_t launch_query_suffix(int d, const BwdArgs& a, hipStream_t s);
 hipError_t launch_geometry(int cal, int rec, const GeoArgs& a, hipStream_t s);
 hipError_t launch_tiles_to_dense(int BH, int T, const float* tiles, int key_major, float* dense,
                                  hipStream_t s);

@@ -424,6 +424,10 @@ class SliceCheck:
         bad = []
         for t in self.rows:
             row = g["dS"][t, : t + 1].astype(np.float64)
+            if self.p.grad_rule == O.P1:
+                # P1 stores the detached gradient; the row mean (cm) is taken
+                # off through dQ and dK, so the projected row is dS - cm
+                row = row - float(g["cm"][t])
             l1 = np.abs(row).sum()
             floor = 0.0
             fw = self.ref["rows"][t][0]

@@ -50,9 +50,14 @@ def zero_sum_all_rows(g, params, tol=1e-5):
     gradient cancels only to the rounding of two dot products; single-key rows
     have dS = 0 and pass anyway)."""
     import torch
-    dS = g["dS"]
-    sums = dS.double().sum(-1)
-    l1 = dS.double().abs().sum(-1)
+    dS = g["dS"].double()
+    if params.grad_rule == "p1":
+        # the stored detached gradient minus the row mean on the causal keys
+        T = dS.shape[-1]
+        causal = torch.ones(T, T, dtype=torch.bool, device=dS.device).tril()
+        dS = dS - g["cm"].double()[..., None] * causal
+    sums = dS.sum(-1)
+    l1 = dS.abs().sum(-1)
     bad = sums.abs() > tol * l1
     if params.calibration == "minmax" and params.reconstruction not in ("exact", "exp_bf16", "exp_fp8"):
         bad &= (g["m"] - g["n"]).double() >= 1e-12

@@ -89,7 +89,7 @@ def test_small_d128(cal, rec, ste):
 @pytest.mark.parametrize("cal,rec,ste", [("minmax", "lerp", "weight"), ("fwm", "nearest", "prob")])
 @pytest.mark.parametrize("rule", RULES)
 def test_small_d128_rules(cal, rec, ste, rule):
-    """Every gradient rule at d = 128 (the P1 prefix sums and centring have
+    """Every gradient rule at d = 128 (the P1 prefix and suffix sums have
     their own per-d code)."""
     check(SMALL128, P(K=16, tau=6.0, calibration=cal, reconstruction=rec, surrogate=ste, grad_rule=rule))
 
