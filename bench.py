@@ -545,6 +545,9 @@ def main():
                    "reconstruction": variant["reconstruction"], "surrogate": variant["surrogate"],
                    "grad_rule": variant["grad_rule"], "flop_per_step": flop_step},
         "pct_mfma_roofline": round(100 * value / PEAK_FP32_MFMA, 2),
+        # the FlashAttention convention counts 14*d flop per causal pair (it
+        # includes the backward's recompute of QK^T, which this path does not do)
+        "tflops_fa_convention": round(value * 14 / 12, 3),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP32_MFMA,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_MFMA, 4), "traffic": traffic,
                      "kernel": dominant, "flop_per_launch": flop_kernel,
