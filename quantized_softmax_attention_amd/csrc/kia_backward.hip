@@ -137,6 +137,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
     // with a compensated (hi, lo) pair.  SB / K enters the two routed terms
     // with opposite signs and cancels exactly, so an fp32 running sum
     // suffices for it.
+    // the argmax entry's final value is formed in the epilogue from the other
+    // keys' direct terms (full and max-only rules)
+    const bool use_max = !rg.degen && (a.rule == GRAD_FULL || a.rule == GRAD_MAX_ONLY);
     float SA = 0.f, SBu = 0.f, SBf = 0.f;
     float SAhi = 0.f, SAlo = 0.f;  // compensated running sum of the per-tile SA
     f32x16 dq[NB];
@@ -189,6 +192,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
                 for (int j = 0; j < 4; ++j) scur[4 * p + j] = sx[p][j];
 
             float ds[16], pr[16];
+            // key a's position in this tile relative to the lane half's first row
+            // (no register index matches when key a lies elsewhere)
+            const int da = (use_max && (ka >> 5) == kt) ? (ka & 31) - 4 * hl : -1;
             auto grads = [&](auto diag_t) {
                 // no contraction: SA must sum exactly the rounded dS values that are
                 // stored, or the routed calibration terms stop cancelling them
@@ -209,7 +215,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
                         else
                             pr[r] = (valid && qvalid) ? round_exp<REC>(fast_exp2((s - rg.m) * kLog2e)) * invW : 0.f;
                         ds[r] = valid ? fmaf(dp[r], gW, ndW) * pw : 0.f;
-                        SA += ds[r];
+                        SA += (acc_row(r, 0) == da) ? 0.f : ds[r];
                         continue;
                     }
                     const float u = (rg.m - s) * rg.invh;
@@ -245,7 +251,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
                     }
                     pr[r] = keep ? pw : 0.f;
                     ds[r] = keep ? Gc : 0.f;
-                    SA += ds[r];
+                    // the argmax key's own direct term stays out of SA (adding 0
+                    // changes no sum): SA is then the other keys' sum exactly
+                    SA += (acc_row(r, 0) == da) ? 0.f : ds[r];
                     if (CAL == CAL_MINMAX) {
                         // dL/dw * Wd with Wd / g = (c/h - 1) u + c f (i + 1); only h = span/K
                         // needs it (in units of dS: divided by c/h after the loop)
@@ -302,7 +310,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
     SBf += __shfl_xor(SBf, 32);
     const float SB = (rg.cohm1 * SBu + rg.c * SBf) * icoh;
     const bool p1 = a.rule == GRAD_P1;
-    const bool use_max = !rg.degen && (a.rule == GRAD_FULL || a.rule == GRAD_MAX_ONLY);
     const bool use_min = !rg.degen && CAL == CAL_MINMAX && (a.rule == GRAD_FULL || a.rule == GRAD_MIN_ONLY);
 
     // the wave's dS tile stores must be visible before it reads and updates them
@@ -310,14 +317,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
 
     // Every value the epilogue reads depends only on (ka, kb), known since the
     // prologue: the reads all go out here, before any of them is used.
-    const float* ta = dstiles + (size_t)(ka >> 5) * kTileElems;
     const int kra = ka & 31;
-    const bool reread = qvalid && use_max && ((kra >> 2) & 1) == hl;
-    float tv[16];
-    if (reread) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tv[r] = ta[kmajor_offset(li, acc_row(r, hl))];
-    }
     float* ea = dstiles + (size_t)(ka >> 5) * kTileElems + kmajor_offset(li, kra);
     float* eb = dstiles + (size_t)(kb >> 5) * kTileElems + kmajor_offset(li, kb & 31);
     float olda = 0.f, oldb = 0.f;
@@ -345,22 +345,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
     // final value is minus the other keys' direct terms (plus SB/K).  Where P
     // is saturated the argmax's own direct term is the fp32 noise of
     // dP - delta, far above the row's true gradient, and adding C_m to it would
-    // cancel that noise only to its rounding.  So the final value is formed
-    // from the other keys alone: the lane half holding key a re-reads its 16
-    // entries of that tile (tv), reproduces the tile's partial sum bit for bit
-    // and replaces it by the partial without key a.
-    // (The noisy partial is taken out of hi first, which is exact, so no
-    // intermediate carries its magnitude into the fp64 rounding.)
-    double sa_lane = (double)SAhi + (double)SAlo;
-    if (reread) {
-        float p_all = 0.f, p_ex = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            p_all += tv[r];
-            p_ex += (acc_row(r, hl) == kra) ? 0.f : tv[r];
-        }
-        sa_lane = (((double)SAhi - (double)p_all) + (double)SAlo) + (double)p_ex;
-    }
+    // cancel that noise only to its rounding.  So the loop leaves that term
+    // out of SA and the final value is formed from the other keys alone.
+    const double sa_lane = (double)SAhi + (double)SAlo;
     const double sa_excl = sa_lane + __shfl_xor(sa_lane, 32);
     double sbk = 0.0;
     if (CAL == CAL_MINMAX) sbk = (double)(SB / rg.Kf);

@@ -101,6 +101,20 @@ __global__ __launch_bounds__(kThreads, (D == 128 && PROB) ? 1 : 2) void kia_forw
             *(f32x4*)(tiles + (size_t)kt_t * kTileElems + p * 256 + lane * 4) = x;
         }
     };
+    // At d = 64 each lane also keeps its 16 scores of the tile where its running
+    // max (min) first appeared (NaN until a tile sets them), so the key index
+    // inside that tile is found from registers.  Re-reading the tile instead
+    // fetches a cache line per lane and tile for 16 bytes of it; at d = 128 the
+    // copies do not fit the register budget and the tile is re-read.
+    constexpr bool KEEP = D == 64;
+    float bx[KEEP ? 16 : 1], by[(KEEP && CAL == CAL_MINMAX) ? 16 : 1];
+    if constexpr (KEEP) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            bx[r] = __builtin_nanf("");
+            if (CAL == CAL_MINMAX) by[r] = __builtin_nanf("");
+        }
+    }
     auto track_tile = [&](const f32x16& acc, int kt_t, bool diag) {
         float x[16], y[16];
 #pragma unroll
@@ -118,10 +132,18 @@ __global__ __launch_bounds__(kThreads, (D == 128 && PROB) ? 1 : 2) void kia_forw
         const bool up = mt > m;
         amt = up ? kt_t : amt;
         m = up ? mt : m;
+        if constexpr (KEEP) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) bx[r] = up ? x[r] : bx[r];
+        }
         if (CAL == CAL_MINMAX) {
             const bool dn = nt < n;
             ant = dn ? kt_t : ant;
             n = dn ? nt : n;
+            if constexpr (KEEP) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) by[r] = dn ? y[r] : by[r];
+            }
         }
     };
     LT::load(lds0, Kp, 0, T, tid);
@@ -189,31 +211,43 @@ __global__ __launch_bounds__(kThreads, (D == 128 && PROB) ? 1 : 2) void kia_forw
         }
     }
     // Row extremes: the two lane halves of a query saw disjoint keys.  Each
-    // half whose extreme equals the row's reads back its 16 stored scores of
-    // the tile where that extreme first appeared and takes the first key
-    // attaining it; the smaller key of the two halves wins.  (The wave's own
-    // score stores precede these loads, so they see the stored values; masked
-    // diagonal entries are excluded by the causal test.)
+    // half whose extreme equals the row's takes the first key attaining it
+    // among its 16 scores of the tile where that extreme first appeared (kept
+    // in registers, or read back: the wave's own score stores precede those
+    // loads, so they see the stored values); the smaller key of the two
+    // halves wins.  Masked diagonal entries are excluded by the causal test.
     {
         const float M = fmaxf(m, __shfl_xor(m, 32));
         const float N = (CAL == CAL_MINMAX) ? fminf(n, __shfl_xor(n, 32)) : 0.f;
         int ia = 0x7fffffff, ib = 0x7fffffff;
         if (active) {
-            f32x4 xa[4], xb[4];
+            float xa[16], xb[16];
+            if constexpr (KEEP) {
 #pragma unroll
-            for (int p = 0; p < 4; ++p) xa[p] = *(const f32x4*)(tiles + (size_t)amt * kTileElems + p * 256 + lane * 4);
-            if (CAL == CAL_MINMAX) {
+                for (int r = 0; r < 16; ++r) {
+                    xa[r] = bx[r];
+                    xb[r] = (CAL == CAL_MINMAX) ? by[r] : 0.f;
+                }
+            } else {
 #pragma unroll
-                for (int p = 0; p < 4; ++p)
-                    xb[p] = *(const f32x4*)(tiles + (size_t)ant * kTileElems + p * 256 + lane * 4);
+                for (int p = 0; p < 4; ++p) {
+                    const f32x4 x = *(const f32x4*)(tiles + (size_t)amt * kTileElems + p * 256 + lane * 4);
+                    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+                    if (CAL == CAL_MINMAX) y = *(const f32x4*)(tiles + (size_t)ant * kTileElems + p * 256 + lane * 4);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        xa[4 * p + j] = x[j];
+                        xb[4 * p + j] = y[j];
+                    }
+                }
             }
 #pragma unroll
             for (int r = 15; r >= 0; --r) {
                 const int ka = amt * kTile + acc_row(r, hl);
-                if (m == M && ka <= qrow && xa[r >> 2][r & 3] == M) ia = ka;
+                if (m == M && ka <= qrow && xa[r] == M) ia = ka;
                 if (CAL == CAL_MINMAX) {
                     const int kb = ant * kTile + acc_row(r, hl);
-                    if (n == N && kb <= qrow && xb[r >> 2][r & 3] == N) ib = kb;
+                    if (n == N && kb <= qrow && xb[r] == N) ib = kb;
                 }
             }
         }
