@@ -101,18 +101,31 @@ __global__ __launch_bounds__(kThreads, (D == 128 && PROB) ? 1 : 2) void kia_forw
             *(f32x4*)(tiles + (size_t)kt_t * kTileElems + p * 256 + lane * 4) = x;
         }
     };
-    // At d = 64 each lane also keeps its 16 scores of the tile where its running
-    // max (min) first appeared (NaN until a tile sets them), so the key index
-    // inside that tile is found from registers.  Re-reading the tile instead
-    // fetches a cache line per lane and tile for 16 bytes of it; at d = 128 the
-    // copies do not fit the register budget and the tile is re-read.
-    constexpr bool KEEP = D == 64;
-    float bx[KEEP ? 16 : 1], by[(KEEP && CAL == CAL_MINMAX) ? 16 : 1];
-    if constexpr (KEEP) {
+    // Each lane keeps its 16 scores of the tile where its running max (min)
+    // first appeared (NaN until a tile sets them), so the key index inside that
+    // tile is found without reading the tile back (a read-back fetches a cache
+    // line per lane for 16 bytes of it).  The interleaved sweep order keeps
+    // them in registers (selects on every tile); the serial order, whose
+    // registers go to d = 128 or the Prob-STE extras, in a per-wave LDS stash
+    // written only when the extreme improves ([extreme][p][lane][4]: the b128
+    // accesses of a wave are conflict-free).
+    float bx[PIPE ? 16 : 1], by[(PIPE && CAL == CAL_MINMAX) ? 16 : 1];
+    __shared__ __attribute__((aligned(16))) float stash[PIPE ? 1 : kWaves * 2 * kTileElems];
+    float* const stw = stash + (PIPE ? 0 : wave * 2 * kTileElems);
+    {
+        const float q = __builtin_nanf("");
+        if constexpr (PIPE) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            bx[r] = __builtin_nanf("");
-            if (CAL == CAL_MINMAX) by[r] = __builtin_nanf("");
+            for (int r = 0; r < 16; ++r) {
+                bx[r] = q;
+                if (CAL == CAL_MINMAX) by[r] = q;
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                *(f32x4*)(stw + p * 256 + lane * 4) = f32x4{q, q, q, q};
+                if (CAL == CAL_MINMAX) *(f32x4*)(stw + kTileElems + p * 256 + lane * 4) = f32x4{q, q, q, q};
+            }
         }
     }
     auto track_tile = [&](const f32x16& acc, int kt_t, bool diag) {
@@ -132,17 +145,26 @@ __global__ __launch_bounds__(kThreads, (D == 128 && PROB) ? 1 : 2) void kia_forw
         const bool up = mt > m;
         amt = up ? kt_t : amt;
         m = up ? mt : m;
-        if constexpr (KEEP) {
+        if constexpr (PIPE) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) bx[r] = up ? x[r] : bx[r];
+        } else if (up) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                *(f32x4*)(stw + p * 256 + lane * 4) = f32x4{x[4 * p], x[4 * p + 1], x[4 * p + 2], x[4 * p + 3]};
         }
         if (CAL == CAL_MINMAX) {
             const bool dn = nt < n;
             ant = dn ? kt_t : ant;
             n = dn ? nt : n;
-            if constexpr (KEEP) {
+            if constexpr (PIPE) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) by[r] = dn ? y[r] : by[r];
+            } else if (dn) {
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+                    *(f32x4*)(stw + kTileElems + p * 256 + lane * 4) =
+                        f32x4{y[4 * p], y[4 * p + 1], y[4 * p + 2], y[4 * p + 3]};
             }
         }
     };
@@ -186,8 +208,8 @@ __global__ __launch_bounds__(kThreads, (D == 128 && PROB) ? 1 : 2) void kia_forw
         else { store_tile(accA, qt, true); track_tile(accA, qt, true); }
     }
     // Sweep 2's first V tile and this wave's first score tiles need no row
-    // statistic: their loads go out here, ahead of the extremes' re-reads
-    // below, so both wait on one memory latency.
+    // statistic: their loads go out here, ahead of the extremes' key search
+    // below.
     float sv[16];
     f32x4 sx[4];
     LT::load(lds0, V, 0, T, tid);
@@ -212,17 +234,16 @@ __global__ __launch_bounds__(kThreads, (D == 128 && PROB) ? 1 : 2) void kia_forw
     }
     // Row extremes: the two lane halves of a query saw disjoint keys.  Each
     // half whose extreme equals the row's takes the first key attaining it
-    // among its 16 scores of the tile where that extreme first appeared (kept
-    // in registers, or read back: the wave's own score stores precede those
-    // loads, so they see the stored values); the smaller key of the two
-    // halves wins.  Masked diagonal entries are excluded by the causal test.
+    // among its 16 kept scores of the tile where that extreme first appeared;
+    // the smaller key of the two halves wins.  Masked diagonal entries hold
+    // -inf / +inf there and are excluded by the causal test as well.
     {
         const float M = fmaxf(m, __shfl_xor(m, 32));
         const float N = (CAL == CAL_MINMAX) ? fminf(n, __shfl_xor(n, 32)) : 0.f;
         int ia = 0x7fffffff, ib = 0x7fffffff;
         if (active) {
             float xa[16], xb[16];
-            if constexpr (KEEP) {
+            if constexpr (PIPE) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     xa[r] = bx[r];
@@ -231,9 +252,9 @@ __global__ __launch_bounds__(kThreads, (D == 128 && PROB) ? 1 : 2) void kia_forw
             } else {
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
-                    const f32x4 x = *(const f32x4*)(tiles + (size_t)amt * kTileElems + p * 256 + lane * 4);
+                    const f32x4 x = *(const f32x4*)(stw + p * 256 + lane * 4);
                     f32x4 y = {0.f, 0.f, 0.f, 0.f};
-                    if (CAL == CAL_MINMAX) y = *(const f32x4*)(tiles + (size_t)ant * kTileElems + p * 256 + lane * 4);
+                    if (CAL == CAL_MINMAX) y = *(const f32x4*)(stw + kTileElems + p * 256 + lane * 4);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         xa[4 * p + j] = x[j];
