@@ -142,6 +142,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
     const bool use_max = !rg.degen && (a.rule == GRAD_FULL || a.rule == GRAD_MAX_ONLY);
     float SA = 0.f, SBu = 0.f, SBf = 0.f;
     float SAhi = 0.f, SAlo = 0.f;  // compensated running sum of the per-tile SA
+    // this query's dS entries at the argmax and argmin keys as the loop stores
+    // them, picked up from the transpose scratch of their tiles
+    float olda = 0.f, oldb = 0.f;
     f32x16 dq[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) dq[b] = f32x16{};
@@ -283,6 +286,12 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
 #pragma unroll
             for (int p = 0; p < 4; ++p)
                 __builtin_nontemporal_store(*(const f32x4*)(xw + li * XS + 8 * p + 4 * hl), (f32x4*)(dd + p * 256 + lane * 4));
+            {
+                // scratch row = key, column = query
+                const float va = xw[(ka & 31) * XS + li], vb = xw[(kb & 31) * XS + li];
+                olda = (kt == (ka >> 5)) ? va : olda;
+                oldb = (kt == (kb >> 5)) ? vb : oldb;
+            }
             __builtin_amdgcn_wave_barrier();
 
             // dQ^T += K^T dS^T : A operand row = head-dim index
@@ -312,18 +321,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
     const bool p1 = a.rule == GRAD_P1;
     const bool use_min = !rg.degen && CAL == CAL_MINMAX && (a.rule == GRAD_FULL || a.rule == GRAD_MIN_ONLY);
 
-    // the wave's dS tile stores must be visible before it reads and updates them
-    __threadfence_block();
-
-    // Every value the epilogue reads depends only on (ka, kb), known since the
-    // prologue: the reads all go out here, before any of them is used.
-    const int kra = ka & 31;
-    float* ea = dstiles + (size_t)(ka >> 5) * kTileElems + kmajor_offset(li, kra);
-    float* eb = dstiles + (size_t)(kb >> 5) * kTileElems + kmajor_offset(li, kb & 31);
-    float olda = 0.f, oldb = 0.f;
-    if (qvalid && use_max) olda = *ea;
-    if (qvalid && use_min && hl == 0) oldb = *eb;
-    // K rows a(t), b(t) and the P1 prefix row; entry i holds columns 8 i + 4 hl .. + 3
+    // K rows a(t), b(t) and the P1 prefix row; entry i holds columns 8 i + 4 hl .. + 3.
+    // Their loads go out first: the wait below covers them and the loop's last
+    // dS stores (the argmax / argmin entries are rewritten after it).
     f32x4 ra[4 * NB], rb[4 * NB], rp[4 * NB];
 #pragma unroll
     for (int i = 0; i < 4 * NB; ++i) {
@@ -337,9 +337,15 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
             const int c = 8 * i + 4 * hl;
             ra[i] = *(const f32x4*)(Kp + (size_t)ka * D + c);
             rb[i] = *(const f32x4*)(Kp + (size_t)kb * D + c);
-            if (p1) rp[i] = *(const f32x4*)(a.prefix_k + head + (size_t)qrow * D + c);
+        }
+        if (p1) {
+#pragma unroll
+            for (int i = 0; i < 4 * NB; ++i)
+                rp[i] = *(const f32x4*)(a.prefix_k + head + (size_t)qrow * D + 8 * i + 4 * hl);
         }
     }
+    float* ea = dstiles + (size_t)(ka >> 5) * kTileElems + kmajor_offset(li, ka & 31);
+    float* eb = dstiles + (size_t)(kb >> 5) * kTileElems + kmajor_offset(li, kb & 31);
 
     // The argmax entry receives C_m = -SA + SB/K (MinMax) or -SA (FWM), so its
     // final value is minus the other keys' direct terms (plus SB/K).  Where P
@@ -355,10 +361,13 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
 
     // P1: the row mean of the detached gradient (0 for a single-key row)
     const float mu = p1 ? (float)(sa_excl / (double)(qrow + 1)) : 0.f;
+    // every store of this wave (the loop's dS tiles included) has completed
+    // before the argmax / argmin entries are rewritten
+    wait_vmcnt<0>();
     if (qvalid) {
         float cm = 0.f;
         if (use_max) {
-            // both lane halves read the loop's direct term (olda); the first writes the final value
+            // both lane halves hold the loop's direct term (olda); the first writes the final value
             const float fin = (float)(sbk - sa_excl);
             cm = fin - olda;  // the routed C_m, as applied on top of the loop's direct term
             if (hl == 0) *ea = fin;
