@@ -453,10 +453,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_cols
             else wait_vmcnt<0>();
             read_tile(pw, lane, pc);
             read_tile(dw, lane, dc);
-            if (prefetch) {
-                wait_lgkm0();
-                dma_pd(qt + 1);
-            }
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 // dO^T and Q^T operands: lane = head-dim column, one float per query
@@ -470,6 +466,15 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_cols
                 for (int kk = 0; kk < 16; ++kk) {
                     dv[b] = mfma32x32x2(xo[kk], pc[kk], dv[b]);
                     dk[b] = mfma32x32x2(xq[kk], dc[kk], dk[b]);
+                    if (b == 0 && kk == 0 && prefetch) {
+                        // the next P / dS tiles reuse the slot once its reads are
+                        // done; waiting here, behind the first products, costs
+                        // less than waiting before them
+                        __builtin_amdgcn_sched_barrier(0);
+                        wait_lgkm0();
+                        dma_pd(qt + 1);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
             }
         }
