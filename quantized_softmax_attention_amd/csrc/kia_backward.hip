@@ -132,13 +132,12 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void kia_backward_rows
     }
 
     // Row sums of the direct term (SA) and of dL/dw * Wd (SB = (c/h - 1) SBu + c SBf).
-    // SA is summed per tile in fp32 (in key order, no contraction, so the
-    // epilogue can reproduce a tile's partial bit for bit) and across tiles
-    // with a compensated (hi, lo) pair.  SB / K enters the two routed terms
-    // with opposite signs and cancels exactly, so an fp32 running sum
-    // suffices for it.
-    // the argmax entry's final value is formed in the epilogue from the other
-    // keys' direct terms (full and max-only rules)
+    // SA is summed per tile in fp32 (in key order, no contraction) and across
+    // tiles with a compensated (hi, lo) pair; under the full and max-only
+    // rules it leaves out the argmax key's own term, since the argmax entry's
+    // final value is formed in the epilogue from the other keys' direct terms.
+    // SB / K enters the two routed terms with opposite signs and cancels
+    // exactly, so an fp32 running sum suffices for it.
     const bool use_max = !rg.degen && (a.rule == GRAD_FULL || a.rule == GRAD_MAX_ONLY);
     float SA = 0.f, SBu = 0.f, SBf = 0.f;
     float SAhi = 0.f, SAlo = 0.f;  // compensated running sum of the per-tile SA
