@@ -291,12 +291,18 @@ def test_repeatable_and_batch_invariant():
 # constructed edge cases
 # ---------------------------------------------------------------------------
 
-def test_exact_ties_pick_lowest_key():
+@pytest.mark.parametrize("d,rec,ste,T", [
+    (64, "lerp", "weight", 70),      # interleaved sweep order: kept copies in registers
+    (128, "lerp", "weight", 70),     # serial order (d = 128): kept copies in LDS
+    (64, "nearest", "prob", 70),     # serial order (Prob-STE)
+    (64, "lerp", "weight", 1100),    # serial order (rows past 32 tiles)
+])
+def test_exact_ties_pick_lowest_key(d, rec, ste, T):
     """Duplicated keys give bitwise-equal scores; the row max and min are
-    attributed to the smallest key index (as in the oracle)."""
+    attributed to the smallest key index (as in the oracle), in both ways the
+    forward keeps the scores of an extreme's tile."""
     import oracle as O
     rng = np.random.default_rng(11)
-    T, d = 70, 64
     q = rng.standard_normal((1, 1, T, d)).astype(np.float32)
     k = rng.standard_normal((1, 1, T, d)).astype(np.float32)
     v = rng.standard_normal((1, 1, T, d)).astype(np.float32)
@@ -310,8 +316,8 @@ def test_exact_ties_pick_lowest_key():
     for t in range(61, T):        # and whose min is the 33 / 60 pair
         q[0, 0, t] -= 4.0 * k[0, 0, 33]
         expect_b[t] = 33
-    params = P(K=8)
-    print("[case] exact ties", flush=True)
+    params = P(K=8, reconstruction=rec, surrogate=ste)
+    print(f"[case] exact ties d={d} {rec}/{ste} T={T}", flush=True)
     g = run_gpu(q, k, v, do, params, want_dense=True, want_idx=False)
     a = g["a"][0, 0].cpu().numpy()
     b = g["b"][0, 0].cpu().numpy()
