@@ -191,7 +191,9 @@ __global__ __launch_bounds__(kThreads, (D == 128 && PROB) ? 1 : 2) void kia_forw
             }
 #pragma unroll
             for (int s = 0; s < D / 2; ++s) acc = mfma32x32x2(xk[s >> 2][s & 3], qf[s], acc);
-            if (kt > 0) pin_interleave<D / 2, 1, D / 8>();
+            // two vector instructions per product where the tracking keeps its
+            // tile copies in registers (about 60 per step), one otherwise
+            if (kt > 0) pin_interleave<D / 2, PIPE ? 2 : 1, D / 8>();
         }
         // the K tile loads were issued first; the 4 score stores may stay in flight
         if (stores) wait_vmcnt<4>();
