@@ -407,10 +407,10 @@ __global__ __launch_bounds__(kThreads, (D == 128 && PROB) ? 1 : 2) void kia_forw
             };
             if (kt + 1 < qt) {
                 interleave<16 * NB, 16>(mstep, [&](int r) { recon(kt + 1, std::false_type{}, r, wn, wln); });
-                pin_interleave<16 * NB, (PROB ? 4 : 6) * 2 / NB, 16 * NB>();
+                pin_interleave<16 * NB, (PROB ? 4 : 5) * 2 / NB, 16 * NB>();
             } else if (kt + 1 == qt) {
                 interleave<16 * NB, 16>(mstep, [&](int r) { recon(kt + 1, std::true_type{}, r, wn, wln); });
-                pin_interleave<16 * NB, (PROB ? 4 : 6) * 2 / NB, 16 * NB>();
+                pin_interleave<16 * NB, (PROB ? 4 : 5) * 2 / NB, 16 * NB>();
             } else {
 #pragma unroll
                 for (int s = 0; s < 16 * NB; ++s) mstep(s);
